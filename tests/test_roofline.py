@@ -1,0 +1,44 @@
+"""Host-side cost model against the pages' worked example (CPU only)."""
+import json
+import os
+
+import pytest
+
+from chunked_prefill_hybrid_rmsnorm_amd import roofline as rl
+from chunked_prefill_hybrid_rmsnorm_amd.inputs import MISTRAL_7B
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "p3_worked_example.json")
+
+
+def _plan(p):
+    return [(b["count"], b["t_math_ms"], b["t_mem_ms"]) for b in p["batches"]]
+
+
+def test_worked_example_totals():
+    g = json.load(open(GOLDEN))
+    a = rl.schedule_time(_plan(g["plan_a"]))
+    b = rl.schedule_time(_plan(g["plan_b"]))
+    assert a == g["plan_a"]["total_ms"]
+    assert b == g["plan_b"]["total_ms"]
+    assert abs((a / b - 1) - g["slower_fraction_approx"]) < 0.05
+
+
+def test_tile_quantization_blocks():
+    g = json.load(open(GOLDEN))["tile_quantization"]
+    assert rl.tiles_needed(g["rows"], g["tile"]) == g["blocks"]
+    assert rl.tiles_needed(256, 128) == 2
+    assert rl.round_up(257, 16) == 272
+
+
+def test_mistral_weight_bytes():
+    s = rl.layer_stages(4096, 32, 8, 128, 14336, [256], [768], [1000] * 32)
+    by = {x.name: x for x in s}
+    w = (by["gemm_qkv"].bytes - 288 * 4096 * 2 - 288 * 6144 * 2
+         + by["gemm_o"].bytes - 288 * 4096 * 2 - 2 * 288 * 4096 * 2
+         + by["gemm_gate_up"].bytes - 288 * 4096 * 2 - 288 * 14336 * 2
+         + by["gemm_down"].bytes - 288 * 14336 * 2 - 2 * 288 * 4096 * 2)
+    assert w == 2 * (6144 * 4096 + 4096 * 4096 + 2 * 14336 * 4096 + 4096 * 14336)
+    assert by["decode_attn"].bytes == 32 * 1001 * MISTRAL_7B.kv_bytes_per_token + 2 * 32 * 4096 * 2
+    # below the ridge (~312 flop/B) the weight-streaming GEMMs are HBM-bound
+    assert by["gemm_gate_up"].bound == "hbm"
+    assert by["decode_attn"].bound == "hbm"
