@@ -1,0 +1,248 @@
+"""Throughput of one hybrid-batch decoder-layer forward on one MI355X.
+
+Workload (default): a Mistral-7B-shaped layer (H=4096, 32 q / 8 kv heads,
+head_dim 128, SwiGLU FFN 14336, bf16 weights N(0, 0.02)) over a hybrid batch
+of chunk 4 of a 1024-token prompt (Lp=256, 768 tokens already cached) plus
+Bd=32 decodes with contexts drawn from U{128..2048}; pages of 16 tokens;
+rows padded to 16.  Synthetic, seeded inputs (seed 0).
+
+A step is one ``hl_layer_forward`` call (every kernel of the layer).  Inputs
+are resident in HBM before the timed region; R copies of the weights and of
+the KV pool are rotated so that the 256 MB MALL cannot hold one call's
+working set for the next.
+
+Printed: one JSON line with tokens/s per layer (real rows / time), the
+dominant kernel's roofline figures, per-kernel times against the roofline
+model T = max(T_math, T_mem), and the CPU oracle's rate on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-batch tokens/s per layer (Lp+Bd); % peak MFMA (linear), % HBM BW (attn)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", choices=["mistral", "llama70", "tiny"], default="mistral")
+    p.add_argument("--pad", type=int, default=16)
+    p.add_argument("--rotate", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-runs", type=int, default=2)
+    return p.parse_args()
+
+
+def make_batch(name):
+    from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
+    if name == "mistral":
+        return I.mistral_batch(seed=0), (
+            "mistral7b-shaped layer: Lp=256 (768 cached) + Bd=32 decodes, ctx U[128,2048]")
+    if name == "llama70":
+        return I.llama70_batch(seed=0), (
+            "llama2-70b-shaped layer: Lp=512 (3584 cached) + Bd=64 decodes, ctx U[512,4096]")
+    return I.tiny_batch(seed=0), "tiny layer H=256: Lp=64 (64 cached) + Bd=4 decodes, ctx U[16,128]"
+
+
+def stage_runners(db, copies, B):
+    """One launcher per kernel, same arguments as inside hl_layer_forward,
+    fed from the rotated copies.  Returns {stage name: fn(i)}."""
+    import torch
+    s = db.shape
+    M, Mp = db.M, db.Mp
+    H, F, nq, nkv, d = s.hidden, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim
+    nqkv = s.qkv_rows
+    dev = db.x.device
+    e = lambda n: torch.empty((Mp, n), dtype=torch.bfloat16, device=dev)
+    xn, qkv, attn, h, act = e(H), e(nqkv), e(nq * d), e(H), e(F)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    pos = torch.empty(M, dtype=torch.int32, device=dev)
+    slot = torch.empty(M, dtype=torch.int32, device=dev)
+    B.hl_slot_mapping(db.cfg, db.chunks, db.dec, db.kv.num_pages, pos, slot)
+    dws = B.hl_decode_workspace_bytes(db.cfg, db.dec.n, db.dec.max_ctx) if db.dec.n else 0
+    dws_t = torch.empty(max(dws, 256), dtype=torch.uint8, device=dev)
+    x = db.x
+    # fill the activations once so every stage reads realistic values
+    w0, kv0 = copies[0]
+    B.hl_rmsnorm(x, w0[0]["g_attn"], xn, M, Mp, H, s.rms_eps)
+    B.hl_gemm_bf16(xn, w0[0]["w_qkv"], qkv, None, M, Mp, nqkv, H)
+    torch.cuda.synchronize()
+    lp = sum(c.length for c in db.hb.chunks)
+
+    def W(i):
+        return copies[i % len(copies)][0][0]
+
+    def KV(i):
+        return copies[i % len(copies)][1]
+
+    return {
+        "rmsnorm1": lambda i: B.hl_rmsnorm(x, W(i)["g_attn"], xn, M, Mp, H, s.rms_eps),
+        "gemm_qkv": lambda i: B.hl_gemm_bf16(xn, W(i)["w_qkv"], qkv, None, M, Mp, nqkv, H),
+        "rope_kv_append": lambda i: B.hl_rope_kv_append(db.cfg, qkv, pos, slot, M, KV(i)),
+        "prefill_attn": lambda i: B.hl_prefill_attention(db.cfg, qkv, db.chunks, KV(i), attn),
+        "decode_attn": lambda i: B.hl_decode_attention(db.cfg, qkv, lp, db.dec, KV(i), attn,
+                                                       dws_t, dws),
+        "gemm_o": lambda i: B.hl_gemm_bf16(attn, W(i)["w_o"], h, x, M, Mp, H, nq * d),
+        "rmsnorm2": lambda i: B.hl_rmsnorm(h, W(i)["g_ffn"], xn, M, Mp, H, s.rms_eps),
+        "gemm_gate_up": lambda i: B.hl_gemm_swiglu(xn, W(i)["w_gate"], W(i)["w_up"], act, Mp, F, H),
+        "gemm_down": lambda i: B.hl_gemm_bf16(act, W(i)["w_down"], out, h, M, Mp, H, F),
+    }
+
+
+def time_loop(fn, steps, warmup):
+    """Average ms per call, HIP events on the current stream (the one the
+    library launches on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(hb, runs):
+    """The oracle as it stands, on the same workload, on the host cores."""
+    import numpy as np
+    from oracle import layer_forward
+    from tests.oracle_inputs import oracle_args
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    args = oracle_args(hb)
+    times = []
+    for _ in range(runs):
+        t = time.perf_counter()
+        layer_forward(*args)
+        times.append(time.perf_counter() - t)
+    t_med = sorted(times)[len(times) // 2]
+    return {"value": hb.x.shape[0] / t_med, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{runs} full calls of the benchmarked hybrid batch "
+                      f"(M={hb.x.shape[0]} rows), float64 numpy oracle, median "
+                      f"{t_med:.2f} s/call; host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("bench.py: only --gpus 1 is supported (single-GPU build)")
+        sys.exit(2)
+    import torch
+    from chunked_prefill_hybrid_rmsnorm_amd import binding as B
+    from chunked_prefill_hybrid_rmsnorm_amd import roofline as RL
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    B.load()
+    torch.cuda.set_device(0)
+
+    log(f"generating {a.workload} inputs ...")
+    hb, desc = make_batch(a.workload)
+    db = B.DeviceBatch(hb, pad=a.pad)
+    log("uploading rotation copies ...")
+    copies = [((db.wt, db.weights), db.kv)]
+    keep = []
+    for _ in range(a.rotate - 1):
+        wt = {k: v.clone() for k, v in db.wt.items()}
+        wstruct = B.hl_weights(*(wt[k].data_ptr() for k in
+                                 ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "g_attn", "g_ffn")))
+        kvt = db.kv_t.clone()
+        keep.append((wt, kvt))
+        copies.append(((wt, wstruct), B.hl_kv(kvt.data_ptr(), db.kv.num_pages)))
+    torch.cuda.synchronize()
+
+    def layer(i):
+        (wt, ws), kv = copies[i % len(copies)]
+        B.hl_layer_forward(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws, db.ws_bytes,
+                           a.pad)
+
+    log(f"layer: {a.warmup} warmup + {a.steps} timed steps ...")
+    ms = time_loop(layer, a.steps, a.warmup)
+    M = db.M
+    tok_s = M / (ms / 1e3)
+    log(f"layer {ms * 1e3:.1f} us/step, {tok_s / 1e6:.3f} M tokens/s")
+
+    # per-kernel times (same kernels, same arguments, rotated weights/KV)
+    runners = stage_runners(db, copies, B)
+    lens = [c.length for c in hb.chunks]
+    starts = [c.start_pos for c in hb.chunks]
+    stages = {s.name: s for s in RL.layer_stages(hb.shape.hidden, hb.shape.n_q_heads,
+                                                  hb.shape.n_kv_heads, hb.shape.head_dim,
+                                                  hb.shape.ffn, lens, starts,
+                                                  [int(c) for c in hb.decodes.ctx_lens], a.pad)}
+    for i, fn in enumerate(runners.values()):  # fill every buffer once, in layer order
+        fn(0)
+    torch.cuda.synchronize()
+    table = {}
+    for name, fn in runners.items():
+        t = time_loop(fn, a.steps, a.warmup) * 1e-3
+        st = stages[name]
+        table[name] = {
+            "us": round(t * 1e6, 2),
+            "bound": st.bound,
+            "t_roof_us": round(st.t_roof() * 1e6, 2),
+            "roof_frac": round(st.t_roof() / t, 4),
+            "GB/s": round(st.bytes / t / 1e9, 1),
+            "TFLOP/s": round(st.flops / t / 1e12, 2),
+        }
+        log(f"  {name:15s} {t * 1e6:8.1f} us  roof {st.t_roof() * 1e6:7.1f} us  "
+            f"({st.bound}, frac {st.t_roof() / t:.3f})")
+    dom = max(table, key=lambda k: table[k]["us"])
+    st = stages[dom]
+    t_dom = table[dom]["us"] * 1e-6
+    if st.bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(st.bytes / t_dom / 1e9, 1),
+                "peak": RL.PEAK_HBM_BPS / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(st.flops / t_dom / 1e12, 2),
+                "peak": RL.PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = st.bytes if st.bound == "hbm" else st.flops
+    t_roof = RL.layer_roofline_time(list(stages.values()))
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "rows": M, "rows_padded": db.Mp, "pad": a.pad,
+                   "rotated_copies": a.rotate},
+        "roofline": roof,
+        "layer_roofline": {"t_roof_us": round(t_roof * 1e6, 2), "t_us": round(ms * 1e3, 2),
+                           "frac": round(t_roof / (ms * 1e-3), 4)},
+        "stages": table,
+    }
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(hb, a.cpu_runs)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

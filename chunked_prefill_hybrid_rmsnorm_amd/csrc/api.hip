@@ -1,0 +1,344 @@
+// C ABI of the hybrid-batch decoder layer: argument checks, workspace
+// layout and the sequence of kernels on the caller's stream.
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace hl;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+int check_config(const hl_config* c) {
+  if (!c) return HL_ERR_NULL;
+  if (c->head_dim != 64 && c->head_dim != 128) return HL_ERR_UNSUPPORTED;
+  if (c->page_size != 16) return HL_ERR_UNSUPPORTED;
+  if (c->hidden <= 0 || c->ffn <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0)
+    return HL_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads) return HL_ERR_SHAPE;
+  if (c->n_q_heads / c->n_kv_heads > 16) return HL_ERR_UNSUPPORTED;
+  if (c->hidden % 64 || c->ffn % 64 || (c->n_q_heads * c->head_dim) % 64) return HL_ERR_SHAPE;
+  return HL_OK;
+}
+
+struct Layout {
+  int Mp;
+  size_t pos, slot, xn1, qkv, attn, h, xn2, act, dec, total;
+};
+
+Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad) {
+  Layout L{};
+  L.Mp = round_up(std::max(rows, 1), pad);
+  const size_t Mp = L.Mp;
+  const size_t H = c->hidden, F = c->ffn, d = c->head_dim;
+  const size_t nqkv = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * d;
+  size_t o = 0;
+  L.pos = o;  o = align256(o + Mp * 4);
+  L.slot = o; o = align256(o + Mp * 4);
+  L.xn1 = o;  o = align256(o + Mp * H * 2);
+  L.qkv = o;  o = align256(o + Mp * nqkv * 2);
+  L.attn = o; o = align256(o + Mp * c->n_q_heads * d * 2);
+  L.h = o;    o = align256(o + Mp * H * 2);
+  L.xn2 = o;  o = align256(o + Mp * H * 2);
+  L.act = o;  o = align256(o + Mp * F * 2);
+  L.dec = o;
+  o = align256(o + (n_dec > 0 ? decode_workspace_bytes(n_dec, c->n_q_heads, d, max_ctx) : 0));
+  L.total = o;
+  return L;
+}
+
+int fill_chunks(const hl_chunk* chunks, int n_chunks, ChunkList* cl) {
+  if (n_chunks < 0) return HL_ERR_SHAPE;
+  if (n_chunks > HL_MAX_CHUNKS) return HL_ERR_UNSUPPORTED;
+  if (n_chunks > 0 && !chunks) return HL_ERR_NULL;
+  memset(cl, 0, sizeof(*cl));
+  cl->n = n_chunks;
+  int row = 0;
+  for (int i = 0; i < n_chunks; ++i) {
+    const hl_chunk& c = chunks[i];
+    if (c.len < 0 || c.start_pos < 0 || c.n_blocks < 0) return HL_ERR_SHAPE;
+    if (c.len > 0 && !c.block_table) return HL_ERR_NULL;
+    cl->c[i] = ChunkDev{c.len, c.start_pos, row, c.n_blocks, c.block_table};
+    row += c.len;
+  }
+  cl->n_rows = row;
+  return HL_OK;
+}
+
+int fill_decodes(const hl_decodes* d, DecDev* dd) {
+  memset(dd, 0, sizeof(*dd));
+  if (!d || d->n == 0) return HL_OK;
+  if (d->n < 0 || d->max_blocks <= 0 || d->max_ctx < 0) return HL_ERR_SHAPE;
+  if (!d->ctx_lens || !d->block_tables) return HL_ERR_NULL;
+  *dd = DecDev{d->n, d->ctx_lens, d->block_tables, d->max_blocks, d->max_ctx};
+  return HL_OK;
+}
+
+KvDev make_kv(const hl_config* c, const hl_kv* kv) {
+  return KvDev{kv->data, kv->num_pages, c->n_kv_heads, c->head_dim, c->page_size};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hl_error_string(int code) {
+  switch (code) {
+    case HL_OK: return "ok";
+    case HL_ERR_NULL: return "required pointer is NULL";
+    case HL_ERR_SHAPE: return "inconsistent or unsupported sizes";
+    case HL_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, page_size, group or chunk count)";
+    case HL_ERR_WORKSPACE: return "workspace too small";
+    case HL_ERR_LAUNCH: return "kernel launch failed";
+    case HL_ERR_METADATA: return "invalid metadata (page id, block table or context length)";
+    case HL_ERR_HIP: return "HIP runtime call failed";
+  }
+  return "unknown error";
+}
+
+int hl_workspace_bytes(const hl_config* cfg, int32_t max_rows, int32_t max_decodes,
+                       int32_t max_ctx, int32_t pad, size_t* bytes) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!bytes) return HL_ERR_NULL;
+  if (max_rows < 0 || max_decodes < 0 || max_ctx < 0 || pad <= 0 || pad % 16) return HL_ERR_SHAPE;
+  *bytes = make_layout(cfg, max_rows, max_decodes, max_ctx, pad).total;
+  return HL_OK;
+}
+
+int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t max_ctx,
+                              size_t* bytes) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!bytes) return HL_ERR_NULL;
+  if (n_decodes < 0 || max_ctx < 0) return HL_ERR_SHAPE;
+  *bytes = decode_workspace_bytes(n_decodes, cfg->n_q_heads, cfg->head_dim, max_ctx);
+  return HL_OK;
+}
+
+int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                     const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                     const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
+                     const hl_taps* taps, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!w || !x || !kv || !out || !ws || !kv->data) return HL_ERR_NULL;
+  if (!w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->g_attn || !w->g_ffn)
+    return HL_ERR_NULL;
+  if (pad <= 0 || pad % 16 || kv->num_pages <= 0) return HL_ERR_SHAPE;
+  if ((const void*)x == (const void*)out) return HL_ERR_SHAPE;
+  ChunkList cl;
+  if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
+  DecDev dd;
+  if ((e = fill_decodes(dec, &dd))) return e;
+  const int M = cl.n_rows + dd.n;
+  if (M == 0) return HL_ERR_SHAPE;
+  const Layout L = make_layout(cfg, M, dd.n, dd.max_ctx, pad);
+  if (ws_bytes < L.total) return HL_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return HL_ERR_WORKSPACE;
+
+  char* base = static_cast<char*>(ws);
+  auto pick = [&](hl_bf16* tap, size_t off) {
+    return tap ? reinterpret_cast<bf16*>(tap) : reinterpret_cast<bf16*>(base + off);
+  };
+  const hl_taps none{};
+  const hl_taps& t = taps ? *taps : none;
+  int32_t* pos = reinterpret_cast<int32_t*>(base + L.pos);
+  int32_t* slot = reinterpret_cast<int32_t*>(base + L.slot);
+  bf16* xn1 = pick(t.xn1, L.xn1);
+  bf16* qkv = pick(t.qkv, L.qkv);
+  bf16* attn = pick(t.attn, L.attn);
+  bf16* h = pick(t.h, L.h);
+  bf16* xn2 = pick(t.xn2, L.xn2);
+  bf16* act = pick(t.act, L.act);
+
+  const int H = cfg->hidden, F = cfg->ffn, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  const int d = cfg->head_dim, Mp = L.Mp;
+  const int nqkv = (nq + 2 * nkv) * d;
+  const KvDev kvd = make_kv(cfg, kv);
+  const bf16* xin = reinterpret_cast<const bf16*>(x);
+
+  hipError_t r;
+#define HL_TRY(call)                      \
+  do {                                    \
+    if ((r = (call)) != hipSuccess) return HL_ERR_LAUNCH; \
+  } while (0)
+  // a0: positions and slots of every row
+  HL_TRY(launch_slot_map(cl, dd, cfg->page_size, kv->num_pages, pos, slot, stream));
+  // a1: RMSNorm (pad rows -> 0)
+  HL_TRY(launch_rmsnorm(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
+                        cfg->rms_eps, stream));
+  // a2: fused QKV projection on the stacked rows
+  HL_TRY(launch_gemm(EPI_STORE, xn1, reinterpret_cast<const bf16*>(w->w_qkv), nullptr, qkv,
+                     nullptr, M, Mp, nqkv, H, stream));
+  // a3: RoPE on q and k, append K and V of every row into its page
+  HL_TRY(launch_rope_kv_append(qkv, pos, slot, M, nq, nkv, d, cfg->rope_theta, kvd, stream));
+  // a4: chunk-prefill attention on rows [0, Lp)
+  HL_TRY(launch_prefill_attention(qkv, nq, nkv, d, cl, kvd, attn, stream));
+  // a5: paged decode attention on rows [Lp, M)
+  HL_TRY(launch_decode_attention(qkv, cl.n_rows, nq, nkv, d, dd, kvd, attn, base + L.dec, stream));
+  // a6: O projection + residual
+  HL_TRY(launch_gemm(EPI_RESIDUAL, attn, reinterpret_cast<const bf16*>(w->w_o), nullptr, h, xin,
+                     M, Mp, H, nq * d, stream));
+  // a7: RMSNorm
+  HL_TRY(launch_rmsnorm(h, reinterpret_cast<const bf16*>(w->g_ffn), xn2, M, Mp, H, cfg->rms_eps,
+                        stream));
+  // a8: gate/up projection + SwiGLU
+  HL_TRY(launch_gemm(EPI_SWIGLU, xn2, reinterpret_cast<const bf16*>(w->w_gate),
+                     reinterpret_cast<const bf16*>(w->w_up), act, nullptr, M, Mp, F, H, stream));
+  // a9: down projection + residual
+  HL_TRY(launch_gemm(EPI_RESIDUAL, act, reinterpret_cast<const bf16*>(w->w_down), nullptr,
+                     reinterpret_cast<bf16*>(out), h, M, Mp, H, F, stream));
+#undef HL_TRY
+  return HL_OK;
+}
+
+int hl_slot_mapping(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,
+                    const hl_decodes* dec, int32_t num_pages, int32_t* positions, int32_t* slots,
+                    hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!positions || !slots) return HL_ERR_NULL;
+  ChunkList cl;
+  if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
+  DecDev dd;
+  if ((e = fill_decodes(dec, &dd))) return e;
+  if (launch_slot_map(cl, dd, cfg->page_size, num_pages, positions, slots, stream) != hipSuccess)
+    return HL_ERR_LAUNCH;
+  return HL_OK;
+}
+
+int hl_validate_metadata(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,
+                         const hl_decodes* dec, int32_t num_pages, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  ChunkList cl;
+  if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
+  DecDev dd;
+  if ((e = fill_decodes(dec, &dd))) return e;
+  if (hipStreamSynchronize(stream) != hipSuccess) return HL_ERR_HIP;
+  const int P = cfg->page_size;
+  std::vector<int> owner(std::max(num_pages, 0), -1);
+  auto claim = [&](int page, int req) {
+    if (page < 0 || page >= num_pages) return false;
+    if (owner[page] != -1 && owner[page] != req) return false;
+    owner[page] = req;
+    return true;
+  };
+  int req = 0;
+  for (int i = 0; i < cl.n; ++i, ++req) {
+    const ChunkDev& c = cl.c[i];
+    const int need = (c.start_pos + c.len + P - 1) / P;
+    if (need > c.n_blocks) return HL_ERR_METADATA;
+    if (need == 0) continue;
+    std::vector<int32_t> bt(need);
+    if (hipMemcpy(bt.data(), c.block_table, need * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return HL_ERR_HIP;
+    for (int b = 0; b < need; ++b)
+      if (!claim(bt[b], req)) return HL_ERR_METADATA;
+  }
+  if (dd.n > 0) {
+    std::vector<int32_t> ctx(dd.n), bts((size_t)dd.n * dd.max_blocks);
+    if (hipMemcpy(ctx.data(), dd.ctx_lens, dd.n * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(bts.data(), dd.block_tables, bts.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return HL_ERR_HIP;
+    for (int j = 0; j < dd.n; ++j, ++req) {
+      if (ctx[j] < 0 || ctx[j] > dd.max_ctx) return HL_ERR_METADATA;
+      const int need = ctx[j] / P + 1;
+      if (need > dd.max_blocks) return HL_ERR_METADATA;
+      for (int b = 0; b < need; ++b)
+        if (!claim(bts[(size_t)j * dd.max_blocks + b], req)) return HL_ERR_METADATA;
+    }
+  }
+  return HL_OK;
+}
+
+int hl_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows, int32_t rows_padded,
+               int32_t hidden, float eps, hipStream_t stream) {
+  if (!x || !g || !y) return HL_ERR_NULL;
+  if (rows < 0 || rows_padded < rows || hidden <= 0 || hidden % 8) return HL_ERR_SHAPE;
+  return launch_rmsnorm(reinterpret_cast<const bf16*>(x), reinterpret_cast<const bf16*>(g),
+                        reinterpret_cast<bf16*>(y), rows, rows_padded, hidden, eps, stream) ==
+                 hipSuccess
+             ? HL_OK
+             : HL_ERR_LAUNCH;
+}
+
+int hl_gemm_bf16(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
+                 int32_t m, int32_t m_padded, int32_t n, int32_t k, hipStream_t stream) {
+  if (!a || !w || !c) return HL_ERR_NULL;
+  if (m < 0 || m_padded < m || m_padded % 16 || n <= 0 || n % 64 || k <= 0 || k % 64)
+    return HL_ERR_SHAPE;
+  const GemmEpilogue epi = residual ? EPI_RESIDUAL : EPI_STORE;
+  return launch_gemm(epi, reinterpret_cast<const bf16*>(a), reinterpret_cast<const bf16*>(w),
+                     nullptr, reinterpret_cast<bf16*>(c), reinterpret_cast<const bf16*>(residual),
+                     m, m_padded, n, k, stream) == hipSuccess
+             ? HL_OK
+             : HL_ERR_LAUNCH;
+}
+
+int hl_gemm_swiglu(const hl_bf16* a, const hl_bf16* w_gate, const hl_bf16* w_up, hl_bf16* act,
+                   int32_t m_padded, int32_t f, int32_t k, hipStream_t stream) {
+  if (!a || !w_gate || !w_up || !act) return HL_ERR_NULL;
+  if (m_padded < 0 || m_padded % 16 || f <= 0 || f % 64 || k <= 0 || k % 64) return HL_ERR_SHAPE;
+  return launch_gemm(EPI_SWIGLU, reinterpret_cast<const bf16*>(a),
+                     reinterpret_cast<const bf16*>(w_gate), reinterpret_cast<const bf16*>(w_up),
+                     reinterpret_cast<bf16*>(act), nullptr, m_padded, m_padded, f, k, stream) ==
+                 hipSuccess
+             ? HL_OK
+             : HL_ERR_LAUNCH;
+}
+
+int hl_rope_kv_append(const hl_config* cfg, hl_bf16* qkv, const int32_t* positions,
+                      const int32_t* slots, int32_t rows, const hl_kv* kv, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!qkv || !positions || !slots || !kv || !kv->data) return HL_ERR_NULL;
+  if (rows < 0) return HL_ERR_SHAPE;
+  return launch_rope_kv_append(reinterpret_cast<bf16*>(qkv), positions, slots, rows,
+                               cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rope_theta,
+                               make_kv(cfg, kv), stream) == hipSuccess
+             ? HL_OK
+             : HL_ERR_LAUNCH;
+}
+
+int hl_prefill_attention(const hl_config* cfg, const hl_bf16* qkv, const hl_chunk* chunks,
+                         int32_t n_chunks, const hl_kv* kv, hl_bf16* attn, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!qkv || !kv || !kv->data || !attn) return HL_ERR_NULL;
+  ChunkList cl;
+  if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
+  return launch_prefill_attention(reinterpret_cast<const bf16*>(qkv), cfg->n_q_heads,
+                                  cfg->n_kv_heads, cfg->head_dim, cl, make_kv(cfg, kv),
+                                  reinterpret_cast<bf16*>(attn), stream) == hipSuccess
+             ? HL_OK
+             : HL_ERR_LAUNCH;
+}
+
+int hl_decode_attention(const hl_config* cfg, const hl_bf16* qkv, int32_t row0,
+                        const hl_decodes* dec, const hl_kv* kv, hl_bf16* attn, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!qkv || !kv || !kv->data || !attn) return HL_ERR_NULL;
+  DecDev dd;
+  if ((e = fill_decodes(dec, &dd))) return e;
+  if (row0 < 0) return HL_ERR_SHAPE;
+  if (dd.n == 0) return HL_OK;
+  if (!ws) return HL_ERR_NULL;
+  if (ws_bytes < decode_workspace_bytes(dd.n, cfg->n_q_heads, cfg->head_dim, dd.max_ctx))
+    return HL_ERR_WORKSPACE;
+  return launch_decode_attention(reinterpret_cast<const bf16*>(qkv), row0, cfg->n_q_heads,
+                                 cfg->n_kv_heads, cfg->head_dim, dd, make_kv(cfg, kv),
+                                 reinterpret_cast<bf16*>(attn), ws, stream) == hipSuccess
+             ? HL_OK
+             : HL_ERR_LAUNCH;
+}
+
+}  // extern "C"

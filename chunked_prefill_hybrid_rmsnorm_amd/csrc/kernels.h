@@ -1,0 +1,40 @@
+// Internal launchers shared by the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+#include "common.h"
+
+namespace hl {
+
+struct DecDev {
+  int32_t n;
+  const int32_t* ctx_lens;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t max_ctx;
+};
+
+// positions / slots of rows [0, chunks.n_rows + dec.n)
+hipError_t launch_slot_map(const ChunkList& chunks, const DecDev& dec, int page_size,
+                           int num_pages, int32_t* pos, int32_t* slot, hipStream_t s);
+
+hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* y, int rows, int rows_padded,
+                          int hidden, float eps, hipStream_t s);
+
+enum GemmEpilogue { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
+// c = a w^T (+ residual) / swiglu(a w_gate^T, a w_up^T).
+hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
+                       const bf16* residual, int m, int m_padded, int n, int k, hipStream_t s);
+
+hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* slot, int rows,
+                                 int nq, int nkv, int d, float theta, const KvDev& kv,
+                                 hipStream_t s);
+
+hipError_t launch_prefill_attention(const bf16* qkv, int nq, int nkv, int d,
+                                    const ChunkList& chunks, const KvDev& kv, bf16* attn,
+                                    hipStream_t s);
+
+size_t decode_workspace_bytes(int n_decodes, int nq, int d, int max_ctx);
+hipError_t launch_decode_attention(const bf16* qkv, int row0, int nq, int nkv, int d,
+                                   const DecDev& dec, const KvDev& kv, bf16* attn, void* ws,
+                                   hipStream_t s);
+
+}  // namespace hl

@@ -1,0 +1,212 @@
+/*
+ * hybrid_layer.h -- C ABI of the MI355X (gfx950) hybrid-batch decoder layer.
+ *
+ * One call runs one pre-norm GQA decoder layer over a *hybrid batch*: the
+ * rows of one or more prefill chunks followed by one row per piggybacked
+ * decode, stacked into a single [M = Lp + Bd, H] matrix.
+ *
+ * Where the operation comes from (pages on SARATHI / Sarathi-Serve):
+ *  - chunked prefill: a prompt is cut into fixed-size chunks computed over
+ *    several iterations; each chunk must attend to the KV of the earlier
+ *    chunks (intelliparadigm.com article, section 3.1; Sarathi-Serve digest,
+ *    section 2, Q2 item 1);
+ *  - decode-maximal batching: one chunk plus decodes form one batch
+ *    (intelliparadigm.com section 3.2; SARATHI summary on gitcode.csdn.net,
+ *    part 2 item 2);
+ *  - the linear layers run once on the concatenated [Lp+Bd, H] matrix,
+ *    attention is split by pointer offset into the prefill part and the
+ *    paged decode part, and results land in preallocated contiguous memory
+ *    for the next layer (gitcode.csdn.net part 2 item 3,
+ *    "merge / split / merge"; intelliparadigm.com section 3.3);
+ *  - each chunk keeps its own position ids so positions run on across
+ *    chunks (intelliparadigm.com section 6.1);
+ *  - the hybrid batch rows are padded to a tile multiple with dummy rows
+ *    (intelliparadigm.com section 4.3; gitcode.csdn.net part 3 item 3).
+ *
+ * Conventions shared by every entry point:
+ *  - bf16 values are passed as uint16_t bit patterns (hl_bf16);
+ *  - every pointer to data is a DEVICE pointer owned by the caller unless
+ *    stated otherwise; the library allocates nothing, frees nothing and keeps
+ *    no pointer after it returns; it holds no mutable global state, so calls
+ *    on different streams with different workspaces may run concurrently;
+ *  - calls only enqueue work on `stream` (0 = the null stream) and return;
+ *    none synchronises except hl_validate_metadata;
+ *  - return value: HL_OK (0) or a negative HL_ERR_* code; nothing is
+ *    enqueued when a check fails; no exception crosses the ABI.
+ */
+#ifndef HYBRID_LAYER_H
+#define HYBRID_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HL_OK 0
+#define HL_ERR_NULL (-1)        /* a required pointer is NULL */
+#define HL_ERR_SHAPE (-2)       /* sizes inconsistent or not multiples the kernels need */
+#define HL_ERR_UNSUPPORTED (-3) /* head_dim not 64/128, page_size not 16, too many chunks */
+#define HL_ERR_WORKSPACE (-4)   /* ws_bytes smaller than hl_workspace_bytes() */
+#define HL_ERR_LAUNCH (-5)      /* a kernel launch failed (hipGetLastError) */
+#define HL_ERR_METADATA (-6)    /* hl_validate_metadata found a bad table entry */
+#define HL_ERR_HIP (-7)         /* a HIP runtime call failed */
+
+#define HL_MAX_CHUNKS 16
+
+typedef uint16_t hl_bf16;
+
+/* Layer shape.  hidden, ffn and n_q_heads*head_dim must be multiples of 64;
+ * n_q_heads a multiple of n_kv_heads; head_dim 64 or 128; page_size 16. */
+typedef struct {
+  int32_t hidden, n_q_heads, n_kv_heads, head_dim, ffn, page_size;
+  float rms_eps;    /* added to mean(x^2) inside the square root */
+  float rope_theta; /* RoPE base */
+} hl_config;
+
+/* Layer weights, bf16, every matrix [out, in] row-major (the GEMMs compute
+ * y = x W^T).  w_qkv stacks n_q_heads q heads, then n_kv_heads k heads, then
+ * n_kv_heads v heads, head_dim rows each. */
+typedef struct {
+  const hl_bf16* w_qkv;  /* [(nq + 2 nkv) d, H] */
+  const hl_bf16* w_o;    /* [H, nq d] */
+  const hl_bf16* w_gate; /* [F, H] */
+  const hl_bf16* w_up;   /* [F, H] */
+  const hl_bf16* w_down; /* [H, F] */
+  const hl_bf16* g_attn; /* [H] RMSNorm gain before attention */
+  const hl_bf16* g_ffn;  /* [H] RMSNorm gain before the FFN */
+} hl_weights;
+
+/* One prefill chunk: `len` rows holding positions start_pos .. start_pos+len-1
+ * of one request.  block_table (device, int32 [n_blocks]) maps position p to
+ * page block_table[p / page_size]; it must cover positions [0, start_pos+len):
+ * tokens before start_pos are already cached (earlier chunks). */
+typedef struct {
+  int32_t len;
+  int32_t start_pos;
+  const int32_t* block_table;
+  int32_t n_blocks;
+} hl_chunk;
+
+/* Piggybacked decodes, one row each.  Decode j has ctx_lens[j] cached tokens;
+ * its new token sits at position ctx_lens[j], is appended there and attends
+ * ctx_lens[j] + 1 keys.  block_tables is device int32 [n, max_blocks].
+ * max_ctx is a HOST-side upper bound of ctx_lens (sizes the split-K grid
+ * without a device read); keys beyond ceil((max_ctx+1)/256)*256 are not
+ * visited, so an underestimate gives wrong results, never a fault. */
+typedef struct {
+  int32_t n;
+  const int32_t* ctx_lens;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t max_ctx;
+} hl_decodes;
+
+/* Paged KV cache of one layer (device).  num_pages pages; page layout bf16:
+ *   K: [n_kv][page_size][head_dim]  token-major,
+ *   V: [n_kv][head_dim][page_size]  dimension-major (V transposed per page),
+ * K block first, then V block: 2 * n_kv * page_size * head_dim per page.
+ * K is stored after the rotary embedding.  Updated in place. */
+typedef struct {
+  hl_bf16* data;
+  int32_t num_pages;
+} hl_kv;
+
+/* Optional intermediate buffers (device, nullable).  A non-NULL pointer
+ * replaces the workspace region of that intermediate, so the caller sees it
+ * without a copy.  Rows: Mp = M rounded up to `pad`.
+ *   xn1 [Mp, H], qkv [Mp, (nq+2nkv) d] (q and k after RoPE), attn [Mp, nq d],
+ *   h [Mp, H] (rows >= M unwritten), xn2 [Mp, H], act [Mp, F]. */
+typedef struct {
+  hl_bf16 *xn1, *qkv, *attn, *h, *xn2, *act;
+} hl_taps;
+
+/* Text for an HL_* code (static storage). */
+const char* hl_error_string(int code);
+
+/* Bytes of workspace hl_layer_forward needs for at most max_rows rows
+ * (chunk rows + decodes), max_decodes decodes with contexts up to max_ctx, and
+ * row padding `pad` (positive multiple of 16).  Host only. */
+int hl_workspace_bytes(const hl_config* cfg, int32_t max_rows, int32_t max_decodes,
+                       int32_t max_ctx, int32_t pad, size_t* bytes);
+
+/* One decoder-layer forward over the hybrid batch.
+ *   x   [M, H] input rows: chunk rows in chunk order, then one row per decode;
+ *   out [M, H] output rows (must not alias x);
+ *   ws  device workspace of ws_bytes >= hl_workspace_bytes(cfg, M, dec->n,
+ *       dec->max_ctx, pad), 256-byte aligned;
+ *   pad row padding: the GEMMs run on Mp = ceil(M/pad)*pad rows, the pad rows
+ *       being zero dummy tokens that write no KV and reach no output.
+ * Steps, all on `stream`: positions and KV slots; RMSNorm; fused QKV GEMM;
+ * RoPE on q and k + append of K/V into the pages; chunk-prefill attention
+ * (causal within the chunk, paged KV of earlier chunks); paged split-K
+ * decode attention; O GEMM + residual; RMSNorm; gate/up GEMM + SwiGLU; down
+ * GEMM + residual.  Writes exactly M KV slots. */
+int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                     const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                     const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
+                     const hl_taps* taps, hipStream_t stream);
+
+/* Row positions and KV slots of a hybrid batch (PagedAttention addressing:
+ * slot = block_table[pos / page_size] * page_size + pos % page_size).
+ * positions, slots: device int32 [M], M = sum of chunk lens + dec->n.  A row
+ * whose block-table index is out of range gets slot -1. */
+int hl_slot_mapping(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,
+                    const hl_decodes* dec, int32_t num_pages, int32_t* positions,
+                    int32_t* slots, hipStream_t stream);
+
+/* Debug check of the metadata (synchronises `stream`, copies the tables to
+ * the host): every page id needed is in [0, num_pages), block tables are long
+ * enough, ctx_lens <= max_ctx, and no two requests share a page. */
+int hl_validate_metadata(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,
+                         const hl_decodes* dec, int32_t num_pages, hipStream_t stream);
+
+/* ---- single steps, same kernels as hl_layer_forward (for per-step checks) */
+
+/* y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g for r < rows; y[r] = 0 for
+ * rows <= r < rows_padded.  x [rows, hidden], y [rows_padded, hidden]. */
+int hl_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
+               int32_t rows_padded, int32_t hidden, float eps, hipStream_t stream);
+
+/* c[m, n] = sum_k a[m, k] w[n, k] (+ residual[m, n]) in fp32, rounded to bf16.
+ * a [m_padded, k], w [n, k], c and residual [*, n] row-major.  Without a
+ * residual all m_padded rows are written; with one only the first m rows.
+ * k multiple of 64, n multiple of 64, m_padded multiple of 16. */
+int hl_gemm_bf16(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
+                 int32_t m, int32_t m_padded, int32_t n, int32_t k, hipStream_t stream);
+
+/* act[m, f] = silu(sum_k a[m,k] w_gate[f,k]) * sum_k a[m,k] w_up[f,k] for
+ * m < m_padded; silu(z) = z / (1 + exp(-z)).  a [m_padded, k],
+ * w_gate/w_up [f, k], act [m_padded, f]. */
+int hl_gemm_swiglu(const hl_bf16* a, const hl_bf16* w_gate, const hl_bf16* w_up, hl_bf16* act,
+                   int32_t m_padded, int32_t f, int32_t k, hipStream_t stream);
+
+/* RoPE on the q and k heads of qkv rows [0, rows) at positions[r] (rotate-half
+ * pairing of element i with i + d/2, angle pos * theta^(-2i/d)), written back
+ * in place, and append of K (rotated) and V into kv at slots[r] (rows with
+ * slot -1 are skipped).  qkv [rows, (nq + 2nkv) d]. */
+int hl_rope_kv_append(const hl_config* cfg, hl_bf16* qkv, const int32_t* positions,
+                      const int32_t* slots, int32_t rows, const hl_kv* kv, hipStream_t stream);
+
+/* Chunk-prefill attention.  Chunk c's rows start at row sum_{i<c} len_i of
+ * qkv (q already rotated, its own K/V already appended); row i of the chunk
+ * (position start_pos + i) attends keys 0 .. start_pos + i through the
+ * chunk's block table.  Writes attn rows of the chunks ([*, nq d]). */
+int hl_prefill_attention(const hl_config* cfg, const hl_bf16* qkv, const hl_chunk* chunks,
+                         int32_t n_chunks, const hl_kv* kv, hl_bf16* attn, hipStream_t stream);
+
+/* Paged decode attention, split-K over 256-key partitions plus a merge.
+ * Decode j reads its q from qkv row row0 + j and writes attn row row0 + j.
+ * ws needs hl_decode_workspace_bytes(). */
+int hl_decode_attention(const hl_config* cfg, const hl_bf16* qkv, int32_t row0,
+                        const hl_decodes* dec, const hl_kv* kv, hl_bf16* attn, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t max_ctx,
+                              size_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYBRID_LAYER_H */

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/hybrid_layer.h declares, and rejects bad arguments before touching
+the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_prefill_hybrid_rmsnorm_amd import binding as B
+from chunked_prefill_hybrid_rmsnorm_amd.inputs import MISTRAL_7B, TINY
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hybrid_layer.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hl_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        from chunked_prefill_hybrid_rmsnorm_amd.build import build
+        build()
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_error_strings(lib):
+    for code in range(0, -8, -1):
+        assert B.error_string(code) not in ("", "unknown error")
+    assert B.error_string(-99) == "unknown error"
+
+
+def test_workspace_bytes_host_only(lib):
+    cfg = B.make_config(MISTRAL_7B)
+    ws = B.hl_workspace_bytes(cfg, 288, 32, 2048, 16)
+    # activations alone: xn1, xn2, h [Mp,H], qkv, attn, act, all bf16
+    acts = 288 * 2 * (3 * 4096 + 6144 + 4096 + 14336)
+    assert ws >= acts
+    assert ws > B.hl_workspace_bytes(cfg, 288, 0, 0, 16)
+    assert B.hl_workspace_bytes(cfg, 257, 0, 0, 256) > B.hl_workspace_bytes(cfg, 257, 0, 0, 16)
+
+
+def _cfg(**kw):
+    c = B.make_config(TINY)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), -3), (dict(page_size=32), -3), (dict(n_kv_heads=3), -2),
+    (dict(hidden=100), -2), (dict(ffn=1000), -2), (dict(n_q_heads=32, n_kv_heads=1), -3),
+])
+def test_config_errors(lib, kw, code):
+    out = ctypes.c_size_t(0)
+    assert lib.hl_workspace_bytes(ctypes.byref(_cfg(**kw)), 10, 1, 10, 16, ctypes.byref(out)) == code
+
+
+def test_bad_pad_and_null(lib):
+    out = ctypes.c_size_t(0)
+    cfg = _cfg()
+    assert lib.hl_workspace_bytes(ctypes.byref(cfg), 10, 1, 10, 24, ctypes.byref(out)) == -2
+    assert lib.hl_workspace_bytes(None, 10, 1, 10, 16, ctypes.byref(out)) == -1
+    assert lib.hl_workspace_bytes(ctypes.byref(cfg), 10, 1, 10, 16, None) == -1
+
+
+def test_layer_forward_rejects_before_launch(lib):
+    """Every failing check returns before a kernel is enqueued (fake,
+    never-dereferenced pointers are safe here)."""
+    cfg = _cfg()
+    fake = 0x1000
+    w = B.hl_weights(*([fake] * 7))
+    kv = B.hl_kv(fake, 10)
+    ch = (B.hl_chunk * 1)(B.hl_chunk(4, 0, fake, 1))
+    dec = B.hl_decodes(0, None, None, 0, 0)
+    f = lib.hl_layer_forward
+    # workspace too small
+    assert f(ctypes.byref(cfg), ctypes.byref(w), fake, ch, 1, ctypes.byref(dec), ctypes.byref(kv),
+             fake + 4096, fake, 16, 16, None, None) == -4
+    # x aliases out
+    assert f(ctypes.byref(cfg), ctypes.byref(w), fake, ch, 1, ctypes.byref(dec), ctypes.byref(kv),
+             fake, fake, 1 << 30, 16, None, None) == -2
+    # no rows
+    empty = (B.hl_chunk * 1)(B.hl_chunk(0, 0, fake, 1))
+    assert f(ctypes.byref(cfg), ctypes.byref(w), fake, empty, 1, ctypes.byref(dec),
+             ctypes.byref(kv), fake + 4096, fake, 1 << 30, 16, None, None) == -2
+    # too many chunks
+    many = (B.hl_chunk * 17)(*([B.hl_chunk(1, 0, fake, 1)] * 17))
+    assert f(ctypes.byref(cfg), ctypes.byref(w), fake, many, 17, ctypes.byref(dec),
+             ctypes.byref(kv), fake + 4096, fake, 1 << 30, 16, None, None) == -3
+    # null weight pointer
+    w0 = B.hl_weights(*([fake] * 6 + [0]))
+    assert f(ctypes.byref(cfg), ctypes.byref(w0), fake, ch, 1, ctypes.byref(dec),
+             ctypes.byref(kv), fake + 4096, fake, 1 << 30, 16, None, None) == -1
+    # decode block table missing
+    bad_dec = B.hl_decodes(2, fake, None, 4, 30)
+    assert f(ctypes.byref(cfg), ctypes.byref(w), fake, ch, 1, ctypes.byref(bad_dec),
+             ctypes.byref(kv), fake + 4096, fake, 1 << 30, 16, None, None) == -1
+
+
+def test_kv_layout_roundtrip():
+    import numpy as np
+    rng = np.random.default_rng(0)
+    kv = rng.integers(0, 65535, size=(3, 2, 2, 16, 64), dtype=np.uint16)
+    lib_layout = B.kv_to_library_layout(kv)
+    back = B.kv_from_library_layout(lib_layout, 2, 16, 64)
+    np.testing.assert_array_equal(back, kv)
+    # V of page 1, kv head 1, token 5, dim 7 sits at dim-major offset 7*16+5
+    flat = lib_layout.reshape(3, -1)
+    v_base = 2 * 16 * 64 + 1 * 64 * 16
+    assert flat[1, v_base + 7 * 16 + 5] == kv[1, 1, 1, 5, 7]

@@ -1,0 +1,237 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle on
+the same seeded inputs.  Floating point within 2e-2 * max|ref| per tensor;
+slots, positions and untouched KV bit-exact."""
+import numpy as np
+import pytest
+
+from chunked_prefill_hybrid_rmsnorm_amd import binding as B
+from chunked_prefill_hybrid_rmsnorm_amd.inputs import (
+    MISTRAL_7B, TINY, LayerShape, bf16_bits, make_hybrid_batch, make_prompt_sequence,
+    mistral_batch, tiny_batch)
+from oracle import layer_forward, rmsnorm, silu
+from tests.gpu_helpers import (TOL, assert_close, check_layer, require_gpu, run_gpu, run_oracle,
+                               tap_f64)
+from tests.oracle_inputs import oracle_weights, widen
+
+pytestmark = pytest.mark.gpu
+
+# small shapes exercising head_dim 128 and a group of 8 at tiny sizes
+D128 = LayerShape(512, 4, 1, 128, 1024)
+G8 = LayerShape(512, 8, 1, 64, 512)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- addressing
+@pytest.mark.parametrize("which", ["tiny", "mistral"])
+def test_slot_mapping_bit_exact(which):
+    import torch
+    hb = tiny_batch(seed=1) if which == "tiny" else mistral_batch(seed=1, prior_kv="none")
+    db = B.DeviceBatch(hb)
+    pos = torch.empty(db.M, dtype=torch.int32, device="cuda")
+    slot = torch.empty(db.M, dtype=torch.int32, device="cuda")
+    B.hl_slot_mapping(db.cfg, db.chunks, db.dec, hb.num_pages, pos, slot)
+    torch.cuda.synchronize()
+    from oracle import slot_of
+    P = hb.shape.page_size
+    want_pos, want_slot = [], []
+    for c in hb.chunks:
+        for i in range(c.length):
+            want_pos.append(c.start_pos + i)
+            want_slot.append(slot_of(c.start_pos + i, c.block_table, P))
+    for j, cl in enumerate(hb.decodes.ctx_lens):
+        want_pos.append(int(cl))
+        want_slot.append(slot_of(int(cl), hb.decodes.block_tables[j], P))
+    np.testing.assert_array_equal(pos.cpu().numpy(), want_pos)
+    np.testing.assert_array_equal(slot.cpu().numpy(), want_slot)
+
+
+# ---------------------------------------------------------------- single steps
+def test_rmsnorm_step():
+    import torch
+    rng = np.random.default_rng(3)
+    x = bf16_bits(rng.standard_normal((37, 4096)).astype(np.float32) * 3)
+    g = bf16_bits(rng.uniform(0.5, 1.5, 4096).astype(np.float32))
+    y = torch.empty((48, 4096), dtype=torch.bfloat16, device="cuda")
+    B.hl_rmsnorm(B.bits_to_device(x), B.bits_to_device(g), y, 37, 48, 4096, 1e-5)
+    torch.cuda.synchronize()
+    got = tap_f64(y, 48)
+    assert_close("rmsnorm", got[:37], rmsnorm(widen(x), widen(g), 1e-5))
+    assert np.all(got[37:] == 0)
+
+
+@pytest.mark.parametrize("m,mp,n,k", [(68, 80, 512, 256), (288, 288, 6144, 4096),
+                                      (1, 16, 256, 1024), (257, 272, 4096, 14336)])
+def test_gemm_step(m, mp, n, k):
+    import torch
+    rng = np.random.default_rng(m + n)
+    a = np.zeros((mp, k), np.uint16)
+    a[:m] = bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    w = bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    r = bf16_bits(rng.standard_normal((m, n)).astype(np.float32))
+    ad, wd, rd = B.bits_to_device(a), B.bits_to_device(w), B.bits_to_device(r)
+    c = torch.empty((mp, n), dtype=torch.bfloat16, device="cuda")
+    B.hl_gemm_bf16(ad, wd, c, None, m, mp, n, k)
+    c2 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    B.hl_gemm_bf16(ad, wd, c2, rd, m, mp, n, k)
+    torch.cuda.synchronize()
+    ref = widen(a) @ widen(w).T
+    got = tap_f64(c, mp)
+    assert_close("gemm", got, ref)
+    assert np.all(got[m:] == 0)
+    assert_close("gemm+residual", tap_f64(c2, m), ref[:m] + widen(r))
+
+
+def test_swiglu_step():
+    import torch
+    rng = np.random.default_rng(5)
+    mp, f, k = 96, 1024, 512
+    a = bf16_bits(rng.standard_normal((mp, k)).astype(np.float32))
+    wg = bf16_bits((rng.standard_normal((f, k)) * 0.05).astype(np.float32))
+    wu = bf16_bits((rng.standard_normal((f, k)) * 0.05).astype(np.float32))
+    act = torch.empty((mp, f), dtype=torch.bfloat16, device="cuda")
+    B.hl_gemm_swiglu(B.bits_to_device(a), B.bits_to_device(wg), B.bits_to_device(wu), act, mp, f, k)
+    torch.cuda.synchronize()
+    A = widen(a)
+    ref = silu(A @ widen(wg).T) * (A @ widen(wu).T)
+    assert_close("swiglu", tap_f64(act, mp), ref)
+
+
+# ---------------------------------------------------------------- whole layer
+def test_layer_tiny():
+    _flush("tiny: H=256 4/2 heads d64, Lp=64 after 64 cached + 4 decodes")
+    hb = tiny_batch(seed=0)
+    _, gpu = run_gpu(hb)
+    check_layer(hb, gpu, run_oracle(hb))
+
+
+def test_layer_mistral_full_size():
+    _flush("mistral-shaped: Lp=256 after 768 cached + 32 decodes ctx U[128,2048]")
+    hb = mistral_batch(seed=0, random_gains=True)
+    _, gpu = run_gpu(hb)
+    check_layer(hb, gpu, run_oracle(hb))
+
+
+EDGE = {
+    "decode_only": dict(chunk_lens=[], chunk_starts=[], n_decodes=5, ctx_range=(1, 90)),
+    "prefill_only_ragged": dict(chunk_lens=[37], chunk_starts=[0], n_decodes=0),
+    "ctx_zero_decodes": dict(chunk_lens=[16], chunk_starts=[16], ctx_lens=[0, 0, 15, 16, 31]),
+    "single_row": dict(chunk_lens=[], chunk_starts=[], ctx_lens=[7]),
+    "single_chunk_row": dict(chunk_lens=[1], chunk_starts=[100], n_decodes=0),
+    "two_chunks": dict(chunk_lens=[20, 45], chunk_starts=[0, 70], n_decodes=3),
+    "three_chunks_ragged": dict(chunk_lens=[3, 17, 29], chunk_starts=[5, 0, 33], n_decodes=2),
+    "long_decode_multi_partition": dict(chunk_lens=[8], chunk_starts=[0], ctx_lens=[255, 256, 700, 1300]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_layer_edge_cases(name):
+    _flush(f"edge case {name}")
+    hb = make_hybrid_batch(TINY, seed=21, random_gains=True, **EDGE[name])
+    _, gpu = run_gpu(hb)
+    check_layer(hb, gpu, run_oracle(hb))
+
+
+@pytest.mark.parametrize("shape", [D128, G8], ids=["d128", "group8"])
+def test_layer_other_head_shapes(shape):
+    hb = make_hybrid_batch(shape, chunk_lens=[40], chunk_starts=[30], n_decodes=3,
+                           ctx_range=(200, 600), seed=22, random_gains=True, weight_std=0.03)
+    _, gpu = run_gpu(hb)
+    check_layer(hb, gpu, run_oracle(hb))
+
+
+@pytest.mark.parametrize("pad", [128, 256])
+def test_tile_padding_changes_nothing(pad):
+    """Dummy pad rows must not change any real row (bit-exact)."""
+    hb = make_hybrid_batch(TINY, chunk_lens=[57], chunk_starts=[16], n_decodes=3, seed=23)
+    _, g16 = run_gpu(hb, pad=16)
+    _, gp = run_gpu(hb, pad=pad)
+    np.testing.assert_array_equal(g16["out"], gp["out"])
+    np.testing.assert_array_equal(g16["kv"], gp["kv"])
+    for k in ("xn2", "act"):
+        assert np.all(gp["pad_rows"][k] == 0)
+
+
+def test_repeat_is_deterministic():
+    hb = tiny_batch(seed=24)
+    _, a = run_gpu(hb)
+    _, b = run_gpu(hb)
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["kv"], b["kv"])
+
+
+# ---------------------------------------------------------------- invariants on the GPU
+def _gpu_prompt_in_chunks(seq, n_chunks):
+    """Prefill the prompt chunk by chunk through the library; the pages carry
+    the state between calls."""
+    import torch
+    from chunked_prefill_hybrid_rmsnorm_amd.inputs import Chunk, Decodes, HybridBatch
+    s = seq.shape
+    wt = B.upload_weights(seq.weights)
+    kv_t = B.bits_to_device(B.kv_to_library_layout(seq.kv_pages))
+    outs = []
+    for k in range(n_chunks):
+        c = seq.chunk(k)
+        hb = HybridBatch(s, seq.weights, seq.chunk_rows(k), [c],
+                         Decodes(np.zeros(0, np.int32), np.zeros((0, 0), np.int32)), seq.kv_pages)
+        db = B.DeviceBatch(hb, weights=wt)
+        db.kv_t = kv_t
+        db.kv = B.hl_kv(kv_t.data_ptr(), seq.kv_pages.shape[0])
+        db.forward()
+        torch.cuda.synchronize()
+        outs.append(tap_f64(db.out, db.M))
+    kv = B.kv_from_library_layout(B.device_to_bits(kv_t), s.n_kv_heads, s.page_size, s.head_dim)
+    return np.concatenate(outs), kv
+
+
+@pytest.mark.parametrize("n_chunks", [2, 4, 8])
+def test_chunked_prefill_equals_unchunked_gpu(n_chunks):
+    seq = make_prompt_sequence(TINY, 256, n_chunks, seed=25, random_gains=True)
+    whole = make_prompt_sequence(TINY, 256, 1, seed=25, random_gains=True)
+    out_c, kv_c = _gpu_prompt_in_chunks(seq, n_chunks)
+    out_1, kv_1 = _gpu_prompt_in_chunks(whole, 1)
+    w = oracle_weights(whole.weights)
+    ref = layer_forward(TINY, w, widen(whole.x_prompt), [(256, 0, whole.block_table)], [], [],
+                        widen(whole.kv_pages))
+    assert_close("chunked vs oracle", out_c, ref.out)
+    assert_close("unchunked vs oracle", out_1, ref.out)
+    # rows are computed independently of how the prompt was cut
+    np.testing.assert_array_equal(out_c, out_1)
+    np.testing.assert_array_equal(kv_c, kv_1)
+
+
+def test_hybrid_equals_each_request_alone_gpu():
+    from chunked_prefill_hybrid_rmsnorm_amd.inputs import Decodes, HybridBatch
+    hb = tiny_batch(seed=26)
+    _, full = run_gpu(hb, taps=False)
+    Lp = hb.chunks[0].length
+    alone_c = HybridBatch(hb.shape, hb.weights, hb.x[:Lp], hb.chunks,
+                          Decodes(np.zeros(0, np.int32), np.zeros((0, 0), np.int32)), hb.kv_pages)
+    _, gc = run_gpu(alone_c, taps=False)
+    np.testing.assert_array_equal(full["out"][:Lp], gc["out"])
+    for j in range(hb.decodes.n):
+        dj = Decodes(hb.decodes.ctx_lens[j:j + 1], hb.decodes.block_tables[j:j + 1])
+        one = HybridBatch(hb.shape, hb.weights, hb.x[Lp + j:Lp + j + 1], [], dj, hb.kv_pages)
+        _, gd = run_gpu(one, taps=False)
+        np.testing.assert_array_equal(full["out"][Lp + j], gd["out"][0])
+
+
+def test_validate_metadata():
+    hb = tiny_batch(seed=27)
+    db = B.DeviceBatch(hb)
+    assert B.hl_validate_metadata(db.cfg, db.chunks, db.dec, hb.num_pages) == 0
+    # a page id past the pool
+    assert B.hl_validate_metadata(db.cfg, db.chunks, db.dec, 3) == -6
+    # two requests sharing a page
+    import torch
+    bad = db.dbt_t.clone()
+    bad[1, 0] = int(hb.chunks[0].block_table[0])
+    dec = B.hl_decodes(db.dec.n, db.dec.ctx_lens, bad.data_ptr(), db.dec.max_blocks, db.dec.max_ctx)
+    assert B.hl_validate_metadata(db.cfg, db.chunks, dec, hb.num_pages) == -6
