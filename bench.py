@@ -75,6 +75,11 @@ def stage_runners(db, copies, B):
     B.hl_slot_mapping(db.cfg, db.chunks, db.dec, db.kv.num_pages, pos, slot)
     dws = B.hl_decode_workspace_bytes(db.cfg, db.dec.n, db.dec.max_ctx) if db.dec.n else 0
     dws_t = torch.empty(max(dws, 256), dtype=torch.uint8, device=dev)
+    pws = B.hl_prefill_workspace_bytes(db.cfg, db.chunks)
+    pws_t = torch.empty(max(pws, 256), dtype=torch.uint8, device=dev)
+    gws = max(B.hl_gemm_workspace_bytes(Mp, n_, k_) for n_, k_ in
+              ((nqkv, H), (H, nq * d), (H, F)))
+    gws_t = torch.empty(max(gws, 256), dtype=torch.uint8, device=dev)
     x = db.x
     # fill the activations once so every stage reads realistic values
     w0, kv0 = copies[0]
@@ -91,15 +96,17 @@ def stage_runners(db, copies, B):
 
     return {
         "rmsnorm1": lambda i: B.hl_rmsnorm(x, W(i)["g_attn"], xn, M, Mp, H, s.rms_eps),
-        "gemm_qkv": lambda i: B.hl_gemm_bf16(xn, W(i)["w_qkv"], qkv, None, M, Mp, nqkv, H),
+        "gemm_qkv": lambda i: B.hl_gemm_bf16(xn, W(i)["w_qkv"], qkv, None, M, Mp, nqkv, H,
+                                             gws_t, gws),
         "rope_kv_append": lambda i: B.hl_rope_kv_append(db.cfg, qkv, pos, slot, M, KV(i)),
-        "prefill_attn": lambda i: B.hl_prefill_attention(db.cfg, qkv, db.chunks, KV(i), attn),
+        "prefill_attn": lambda i: B.hl_prefill_attention(db.cfg, qkv, db.chunks, KV(i), attn,
+                                                         pws_t, pws),
         "decode_attn": lambda i: B.hl_decode_attention(db.cfg, qkv, lp, db.dec, KV(i), attn,
                                                        dws_t, dws),
-        "gemm_o": lambda i: B.hl_gemm_bf16(attn, W(i)["w_o"], h, x, M, Mp, H, nq * d),
+        "gemm_o": lambda i: B.hl_gemm_bf16(attn, W(i)["w_o"], h, x, M, Mp, H, nq * d, gws_t, gws),
         "rmsnorm2": lambda i: B.hl_rmsnorm(h, W(i)["g_ffn"], xn, M, Mp, H, s.rms_eps),
         "gemm_gate_up": lambda i: B.hl_gemm_swiglu(xn, W(i)["w_gate"], W(i)["w_up"], act, Mp, F, H),
-        "gemm_down": lambda i: B.hl_gemm_bf16(act, W(i)["w_down"], out, h, M, Mp, H, F),
+        "gemm_down": lambda i: B.hl_gemm_bf16(act, W(i)["w_down"], out, h, M, Mp, H, F, gws_t, gws),
     }
 
 

@@ -80,13 +80,18 @@ _SIGS = {
     "hl_rmsnorm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32,
                               _c.c_int32, _c.c_float, _c.c_void_p]),
     "hl_gemm_bf16": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32,
-                                _c.c_int32, _c.c_int32, _c.c_int32, _c.c_void_p]),
+                                _c.c_int32, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_size_t,
+                                _c.c_void_p]),
+    "hl_gemm_workspace_bytes": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _P(_c.c_size_t)]),
     "hl_gemm_swiglu": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_int32, _c.c_int32, _c.c_int32, _c.c_void_p]),
     "hl_rope_kv_append": (_c.c_int, [_P(hl_config), _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                      _c.c_int32, _P(hl_kv), _c.c_void_p]),
     "hl_prefill_attention": (_c.c_int, [_P(hl_config), _c.c_void_p, _P(hl_chunk), _c.c_int32,
-                                        _P(hl_kv), _c.c_void_p, _c.c_void_p]),
+                                        _P(hl_kv), _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                        _c.c_void_p]),
+    "hl_prefill_workspace_bytes": (_c.c_int, [_P(hl_config), _P(hl_chunk), _c.c_int32,
+                                              _P(_c.c_size_t)]),
     "hl_decode_attention": (_c.c_int, [_P(hl_config), _c.c_void_p, _c.c_int32, _P(hl_decodes),
                                        _P(hl_kv), _c.c_void_p, _c.c_void_p, _c.c_size_t,
                                        _c.c_void_p]),
@@ -226,9 +231,16 @@ def hl_rmsnorm(x, g, y, rows, rows_padded, hidden, eps, stream=None):
                              _stream(stream)), "hl_rmsnorm")
 
 
-def hl_gemm_bf16(a, w, c, residual, m, m_padded, n, k, stream=None):
+def hl_gemm_workspace_bytes(m_padded, n, k) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().hl_gemm_workspace_bytes(m_padded, n, k, ctypes.byref(out)),
+           "hl_gemm_workspace_bytes")
+    return out.value
+
+
+def hl_gemm_bf16(a, w, c, residual, m, m_padded, n, k, ws=None, ws_bytes=0, stream=None):
     _check(load().hl_gemm_bf16(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), m, m_padded, n, k,
-                               _stream(stream)), "hl_gemm_bf16")
+                               _ptr(ws), ws_bytes, _stream(stream)), "hl_gemm_bf16")
 
 
 def hl_gemm_swiglu(a, w_gate, w_up, act, m_padded, f, k, stream=None):
@@ -241,10 +253,19 @@ def hl_rope_kv_append(cfg, qkv, positions, slots, rows, kv: hl_kv, stream=None):
                                     rows, ctypes.byref(kv), _stream(stream)), "hl_rope_kv_append")
 
 
-def hl_prefill_attention(cfg, qkv, chunks, kv: hl_kv, attn, stream=None):
+def hl_prefill_workspace_bytes(cfg, chunks) -> int:
+    arr, n = _chunk_array(chunks)
+    out = ctypes.c_size_t(0)
+    _check(load().hl_prefill_workspace_bytes(ctypes.byref(cfg), arr, n, ctypes.byref(out)),
+           "hl_prefill_workspace_bytes")
+    return out.value
+
+
+def hl_prefill_attention(cfg, qkv, chunks, kv: hl_kv, attn, ws=None, ws_bytes=0, stream=None):
     arr, n = _chunk_array(chunks)
     _check(load().hl_prefill_attention(ctypes.byref(cfg), _ptr(qkv), arr, n, ctypes.byref(kv),
-                                       _ptr(attn), _stream(stream)), "hl_prefill_attention")
+                                       _ptr(attn), _ptr(ws), ws_bytes, _stream(stream)),
+           "hl_prefill_attention")
 
 
 def hl_decode_attention(cfg, qkv, row0, dec: hl_decodes, kv: hl_kv, attn, ws, ws_bytes,

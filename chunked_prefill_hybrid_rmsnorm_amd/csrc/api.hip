@@ -28,7 +28,7 @@ int check_config(const hl_config* c) {
 
 struct Layout {
   int Mp;
-  size_t pos, slot, xn1, qkv, attn, h, xn2, act, dec, total;
+  size_t pos, slot, xn1, qkv, attn, h, xn2, act, dec, pre, gemm, total;
 };
 
 Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad) {
@@ -48,6 +48,14 @@ Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad
   L.act = o;  o = align256(o + Mp * F * 2);
   L.dec = o;
   o = align256(o + (n_dec > 0 ? decode_workspace_bytes(n_dec, c->n_q_heads, d, max_ctx) : 0));
+  L.pre = o;
+  o = align256(o + prefill_workspace_bound(rows, c->n_q_heads, c->n_kv_heads, (int)d));
+  L.gemm = o;
+  const int nqd = c->n_q_heads * c->head_dim;
+  const size_t g = std::max({gemm_workspace_bytes(EPI_STORE, L.Mp, (int)nqkv, (int)H),
+                             gemm_workspace_bytes(EPI_RESIDUAL, L.Mp, (int)H, nqd),
+                             gemm_workspace_bytes(EPI_RESIDUAL, L.Mp, (int)H, (int)F)});
+  o = align256(o + g);
   L.total = o;
   return L;
 }
@@ -174,26 +182,28 @@ int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x
   HL_TRY(launch_rmsnorm(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
                         cfg->rms_eps, stream));
   // a2: fused QKV projection on the stacked rows
+  void* gws = base + L.gemm;
   HL_TRY(launch_gemm(EPI_STORE, xn1, reinterpret_cast<const bf16*>(w->w_qkv), nullptr, qkv,
-                     nullptr, M, Mp, nqkv, H, stream));
+                     nullptr, gws, M, Mp, nqkv, H, stream));
   // a3: RoPE on q and k, append K and V of every row into its page
   HL_TRY(launch_rope_kv_append(qkv, pos, slot, M, nq, nkv, d, cfg->rope_theta, kvd, stream));
   // a4: chunk-prefill attention on rows [0, Lp)
-  HL_TRY(launch_prefill_attention(qkv, nq, nkv, d, cl, kvd, attn, stream));
+  HL_TRY(launch_prefill_attention(qkv, nq, nkv, d, cl, kvd, attn, base + L.pre, stream));
   // a5: paged decode attention on rows [Lp, M)
   HL_TRY(launch_decode_attention(qkv, cl.n_rows, nq, nkv, d, dd, kvd, attn, base + L.dec, stream));
   // a6: O projection + residual
   HL_TRY(launch_gemm(EPI_RESIDUAL, attn, reinterpret_cast<const bf16*>(w->w_o), nullptr, h, xin,
-                     M, Mp, H, nq * d, stream));
+                     gws, M, Mp, H, nq * d, stream));
   // a7: RMSNorm
   HL_TRY(launch_rmsnorm(h, reinterpret_cast<const bf16*>(w->g_ffn), xn2, M, Mp, H, cfg->rms_eps,
                         stream));
   // a8: gate/up projection + SwiGLU
   HL_TRY(launch_gemm(EPI_SWIGLU, xn2, reinterpret_cast<const bf16*>(w->w_gate),
-                     reinterpret_cast<const bf16*>(w->w_up), act, nullptr, M, Mp, F, H, stream));
+                     reinterpret_cast<const bf16*>(w->w_up), act, nullptr, nullptr, M, Mp, F, H,
+                     stream));
   // a9: down projection + residual
   HL_TRY(launch_gemm(EPI_RESIDUAL, act, reinterpret_cast<const bf16*>(w->w_down), nullptr,
-                     reinterpret_cast<bf16*>(out), h, M, Mp, H, F, stream));
+                     reinterpret_cast<bf16*>(out), h, gws, M, Mp, H, F, stream));
 #undef HL_TRY
   return HL_OK;
 }
@@ -269,15 +279,27 @@ int hl_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows, int
              : HL_ERR_LAUNCH;
 }
 
+int hl_gemm_workspace_bytes(int32_t m_padded, int32_t n, int32_t k, size_t* bytes) {
+  if (!bytes) return HL_ERR_NULL;
+  if (m_padded < 0 || m_padded % 16 || n <= 0 || n % 64 || k <= 0 || k % 64) return HL_ERR_SHAPE;
+  *bytes = std::max(gemm_workspace_bytes(EPI_STORE, m_padded, n, k),
+                    gemm_workspace_bytes(EPI_RESIDUAL, m_padded, n, k));
+  return HL_OK;
+}
+
 int hl_gemm_bf16(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
-                 int32_t m, int32_t m_padded, int32_t n, int32_t k, hipStream_t stream) {
+                 int32_t m, int32_t m_padded, int32_t n, int32_t k, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
   if (!a || !w || !c) return HL_ERR_NULL;
   if (m < 0 || m_padded < m || m_padded % 16 || n <= 0 || n % 64 || k <= 0 || k % 64)
     return HL_ERR_SHAPE;
   const GemmEpilogue epi = residual ? EPI_RESIDUAL : EPI_STORE;
+  const size_t need = gemm_workspace_bytes(epi, m_padded, n, k);
+  if (ws && ws_bytes < need) return HL_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return HL_ERR_WORKSPACE;
   return launch_gemm(epi, reinterpret_cast<const bf16*>(a), reinterpret_cast<const bf16*>(w),
                      nullptr, reinterpret_cast<bf16*>(c), reinterpret_cast<const bf16*>(residual),
-                     m, m_padded, n, k, stream) == hipSuccess
+                     need ? ws : nullptr, m, m_padded, n, k, stream) == hipSuccess
              ? HL_OK
              : HL_ERR_LAUNCH;
 }
@@ -288,7 +310,8 @@ int hl_gemm_swiglu(const hl_bf16* a, const hl_bf16* w_gate, const hl_bf16* w_up,
   if (m_padded < 0 || m_padded % 16 || f <= 0 || f % 64 || k <= 0 || k % 64) return HL_ERR_SHAPE;
   return launch_gemm(EPI_SWIGLU, reinterpret_cast<const bf16*>(a),
                      reinterpret_cast<const bf16*>(w_gate), reinterpret_cast<const bf16*>(w_up),
-                     reinterpret_cast<bf16*>(act), nullptr, m_padded, m_padded, f, k, stream) ==
+                     reinterpret_cast<bf16*>(act), nullptr, nullptr, m_padded, m_padded, f, k,
+                     stream) ==
                  hipSuccess
              ? HL_OK
              : HL_ERR_LAUNCH;
@@ -307,16 +330,32 @@ int hl_rope_kv_append(const hl_config* cfg, hl_bf16* qkv, const int32_t* positio
              : HL_ERR_LAUNCH;
 }
 
+int hl_prefill_workspace_bytes(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,
+                               size_t* bytes) {
+  int e = check_config(cfg);
+  if (e) return e;
+  if (!bytes) return HL_ERR_NULL;
+  ChunkList cl;
+  if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
+  *bytes = prefill_workspace_bytes(cl, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim);
+  return HL_OK;
+}
+
 int hl_prefill_attention(const hl_config* cfg, const hl_bf16* qkv, const hl_chunk* chunks,
-                         int32_t n_chunks, const hl_kv* kv, hl_bf16* attn, hipStream_t stream) {
+                         int32_t n_chunks, const hl_kv* kv, hl_bf16* attn, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   int e = check_config(cfg);
   if (e) return e;
   if (!qkv || !kv || !kv->data || !attn) return HL_ERR_NULL;
   ChunkList cl;
   if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
+  const size_t need = prefill_workspace_bytes(cl, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim);
+  if (ws && ws_bytes < need) return HL_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return HL_ERR_WORKSPACE;
   return launch_prefill_attention(reinterpret_cast<const bf16*>(qkv), cfg->n_q_heads,
                                   cfg->n_kv_heads, cfg->head_dim, cl, make_kv(cfg, kv),
-                                  reinterpret_cast<bf16*>(attn), stream) == hipSuccess
+                                  reinterpret_cast<bf16*>(attn), need ? ws : nullptr,
+                                  stream) == hipSuccess
              ? HL_OK
              : HL_ERR_LAUNCH;
 }

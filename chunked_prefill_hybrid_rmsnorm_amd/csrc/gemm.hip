@@ -3,206 +3,122 @@
 // run once on the stacked chunk + decode rows.
 //
 // Structure (gfx950, wave64):
-//  * a workgroup owns a BM x BN output tile and walks K in steps of 64;
-//    A and W tiles are staged through LDS, double-buffered, with the next
-//    tile's global loads in flight while the current one is multiplied;
-//  * each wave computes C^T = W A^T on its sub-tile with
+//  * a workgroup owns a BM x BN output tile and walks its share of K in
+//    steps of 64; A and W tiles are copied global -> LDS directly
+//    (global_load_lds_dwordx4) into a ring of stages, several k-steps ahead
+//    of the step being multiplied;
+//  * each wave computes C^T = W A^T on a (BM/WM) x (BN/WN) sub-tile with
 //    v_mfma_f32_16x16x32_bf16, so a lane ends up holding four consecutive
-//    output columns of one row and stores them as one 8-byte write;
-//  * workgroups are numbered so that the ones sharing a weight tile land on
-//    the same XCD (workgroup ids are dealt round-robin over the 8 XCDs) and
-//    reuse it from that XCD's L2;
+//    output columns of one row (one 8-byte store);
+//  * at these row counts the weights dominate the traffic, so a tile spans as
+//    many rows as registers allow and the workgroups that share one weight
+//    tile (different row tiles) are numbered to land on the same XCD
+//    (workgroup ids are dealt round-robin over the 8 XCDs) and reuse it from
+//    that XCD's L2;
+//  * narrow outputs split K over several workgroups (fp32 partial tiles in
+//    the workspace, summed in a fixed order by a second kernel, so results
+//    are deterministic);
 //  * epilogues: plain store (QKV), residual add (O and down projections),
-//    SwiGLU (gate and up tiles side by side in one workgroup, combined in
+//    SwiGLU (gate and up rows side by side in one tile, combined in
 //    registers).
-#include "kernels.h"
+#include "gemm_impl.h"
 
 namespace hl {
 
-constexpr int kBK = 64;
-constexpr int kLdsPad = 8;  // bf16 elements of padding per LDS row
-constexpr int kLdsRow = kBK + kLdsPad;
-
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W2,
-    bf16* __restrict__ C, const bf16* __restrict__ R, int M, int Mp, int N, int K, int n_mtiles,
-    int n_ntiles) {
-  constexpr int NT = 64 * WM * WN;
-  constexpr int WTM = BM / WM;  // rows of a wave tile
-  constexpr int WTN = BN / WN;  // LDS W rows of a wave tile
-  constexpr int FM = WTM / 16;
-  constexpr int FN = WTN / 16;
-  constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns per tile
-  constexpr int A_CHUNKS = BM * (kBK / 8) / NT;
-  constexpr int W_CHUNKS = BN * (kBK / 8) / NT;
-  static_assert(BM * (kBK / 8) % NT == 0 && BN * (kBK / 8) % NT == 0, "tile/thread mismatch");
-  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "swiglu needs paired fragments");
-
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * kLdsRow];
-
-  // XCD-aware tile order: XCD x runs a contiguous range of tiles, n-major,
-  // so the m-tiles of one weight tile run together on one XCD.
-  const int total = n_mtiles * n_ntiles;
-  const int b = blockIdx.x;
-  const int per = total / 8, rem = total % 8;
-  const int x = b % 8, s = b / 8;
-  const int tile = x * per + min(x, rem) + s;
-  const int tn = tile / n_mtiles, tm = tile % n_mtiles;
-  const int m0 = tm * BM, n0 = tn * OUT_N;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int l16 = lane & 15, q = lane >> 4;
-
-  u32x4 ra[A_CHUNKS], rw[W_CHUNKS];
-
-  auto load_global = [&](int kt) {
-    const int k0 = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-      const int m = m0 + row;
-      ra[i] = m < Mp ? ld16(A + (size_t)m * K + k0 + kc) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-      const bf16* src;
-      int n;
-      if (EPI == EPI_SWIGLU) {
-        const bool up = row >= BN / 2;
-        n = n0 + (up ? row - BN / 2 : row);
-        src = up ? W2 : W;
-      } else {
-        n = n0 + row;
-        src = W;
-      }
-      rw[i] = n < N ? ld16(src + (size_t)n * K + k0 + kc) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_lds = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&As[st][row * kLdsRow + kc]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Ws[st][row * kLdsRow + kc]) = rw[i];
-    }
-  };
-  // LDS row of the wave's fn-th 16-row W fragment
-  auto w_row = [&](int fn) {
-    if (EPI == EPI_SWIGLU) {
-      constexpr int HALF = FN / 2;
-      return fn < HALF ? wn * (WTN / 2) + fn * 16 : BN / 2 + wn * (WTN / 2) + (fn - HALF) * 16;
-    }
-    return wn * WTN + fn * 16;
-  };
-
-  f32x4 acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int KT = K / kBK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) load_global(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
-      bf16x8 af[FN], bfr[FM];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        af[fn] = as_bf16x8(ld16(&Ws[st][(w_row(fn) + l16) * kLdsRow + ks * 32 + q * 8]));
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        bfr[fm] = as_bf16x8(ld16(&As[st][(wm * WTM + fm * 16 + l16) * kLdsRow + ks * 32 + q * 8]));
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma16x16x32(af[fn], bfr[fm], acc[fn][fm]);
-    }
-    if (kt + 1 < KT) store_lds(st ^ 1);
-    __syncthreads();
+// ------------------------------------------------------------ split-K reduce
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce(const float* __restrict__ part, int splits,
+                                                          bf16* __restrict__ C,
+                                                          const bf16* __restrict__ R, int M, int Mp,
+                                                          int N) {
+  const int n4 = N / 4;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int mlim = EPI == EPI_RESIDUAL ? M : Mp;
+  if (idx >= mlim * n4) return;
+  const int m = idx / n4, n = (idx % n4) * 4;
+  const size_t plane = (size_t)Mp * N;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)m * N + n);
+  for (int z = 1; z < splits; ++z) v += *reinterpret_cast<const f32x4*>(part + z * plane + (size_t)m * N + n);
+  if (EPI == EPI_RESIDUAL) {
+    const u32x2 rr = ld8(R + (size_t)m * N + n);
+    v[0] += __uint_as_float(rr[0] << 16);
+    v[1] += __uint_as_float(rr[0] & 0xffff0000u);
+    v[2] += __uint_as_float(rr[1] << 16);
+    v[3] += __uint_as_float(rr[1] & 0xffff0000u);
   }
-
-  // epilogue: lane holds C[m][n .. n+3] for m = .. + l16, n = .. + 4q
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + wm * WTM + fm * 16 + l16;
-    if (EPI == EPI_SWIGLU) {
-      if (m >= Mp) continue;
-#pragma unroll
-      for (int fn = 0; fn < FN / 2; ++fn) {
-        const int n = n0 + wn * (WTN / 2) + fn * 16 + 4 * q;
-        if (n >= N) continue;
-        const f32x4 g = acc[fn][fm], u = acc[fn + FN / 2][fm];
-        u32x2 o;
-        o[0] = pack2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
-        o[1] = pack2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
-        *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
-      }
-    } else {
-      const int mlim = EPI == EPI_RESIDUAL ? M : Mp;
-      if (m >= mlim) continue;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int n = n0 + wn * WTN + fn * 16 + 4 * q;
-        if (n >= N) continue;
-        f32x4 v = acc[fn][fm];
-        if (EPI == EPI_RESIDUAL) {
-          const u32x2 rr = ld8(R + (size_t)m * N + n);
-          v[0] += __uint_as_float(rr[0] << 16);
-          v[1] += __uint_as_float(rr[0] & 0xffff0000u);
-          v[2] += __uint_as_float(rr[1] << 16);
-          v[3] += __uint_as_float(rr[1] & 0xffff0000u);
-        }
-        u32x2 o;
-        o[0] = pack2(v[0], v[1]);
-        o[1] = pack2(v[2], v[3]);
-        *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
-      }
-    }
-  }
+  u32x2 o;
+  o[0] = pack2(v[0], v[1]);
+  o[1] = pack2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-static hipError_t run_gemm(const bf16* a, const bf16* w, const bf16* w2, bf16* c, const bf16* r,
-                           int m, int mp, int n, int k, hipStream_t s) {
-  constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  const int mt = (mp + BM - 1) / BM, nt = (n + OUT_N - 1) / OUT_N;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(mt * nt), dim3(64 * WM * WN), 0, s,
-                     a, w, w2, c, r, m, mp, n, k, mt, nt);
-  return hipGetLastError();
+// ------------------------------------------------------------ dispatch
+// Row tile: 288 rows (one tile spans a whole hybrid batch of up to 288 rows,
+// so every weight tile is streamed from HBM once) or 128 rows for small
+// batches; 128 weight rows per tile.  K is split so that about one
+// workgroup per CU is resident (measured best on MI355X: 4 waves, 1 per SIMD,
+// with the copy pipeline hiding HBM latency), keeping >= 8 k-steps per split.
+struct Choice {
+  int big;     // 1: 288-row tile, 0: 128-row tile
+  int splits;  // K splits (1 = none)
+};
+
+static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
+  Choice c;
+  c.big = mp > 128 ? 1 : 0;
+  const int bm = c.big ? 288 : 128;
+  const int out_n = epi == EPI_SWIGLU ? 64 : 128;
+  const int tiles = ((mp + bm - 1) / bm) * ((n + out_n - 1) / out_n);
+  const int ksteps = k / kGemmBK;
+  c.splits = 1;
+  if (epi != EPI_SWIGLU)
+    while (tiles * c.splits * 2 <= 256 && ksteps / (c.splits * 2) >= 8 && c.splits < 8) c.splits *= 2;
+  return c;
+}
+
+size_t gemm_workspace_bytes(GemmEpilogue epi, int mp, int n, int k) {
+  const Choice c = choose(epi, mp, n, k);
+  return c.splits > 1 ? (size_t)c.splits * mp * n * sizeof(float) : 0;
+}
+
+template <int EPI>
+static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2,
+                             bf16* c, const bf16* r, float* part, int m, int mp, int n, int k,
+                             hipStream_t s) {
+  if (ch.big) return run_gemm_dma<288, 128, 2, 2, EPI, 3>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  return run_gemm_dma<128, 128, 2, 2, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
 }
 
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
-                       const bf16* residual, int m, int m_padded, int n, int k, hipStream_t s) {
+                       const bf16* residual, void* ws, int m, int m_padded, int n, int k,
+                       hipStream_t s) {
   if (m_padded == 0 || n == 0) return hipSuccess;
+  Choice ch = choose(epi, m_padded, n, k);
+  if (ch.splits > 1 && ws == nullptr) ch.splits = 1;
+  float* part = reinterpret_cast<float*>(ws);
+  hipError_t e;
   switch (epi) {
     case EPI_STORE:
-      return run_gemm<64, 64, 2, 2, EPI_STORE>(a, w, nullptr, c, nullptr, m, m_padded, n, k, s);
+      e = run_choice<EPI_STORE>(ch, a, w, nullptr, c, nullptr, part, m, m_padded, n, k, s);
+      break;
     case EPI_RESIDUAL:
-      return run_gemm<64, 64, 2, 2, EPI_RESIDUAL>(a, w, nullptr, c, residual, m, m_padded, n, k, s);
-    case EPI_SWIGLU:
-      return run_gemm<64, 128, 2, 2, EPI_SWIGLU>(a, w, w2, c, nullptr, m, m_padded, n, k, s);
+      e = run_choice<EPI_RESIDUAL>(ch, a, w, nullptr, c, residual, part, m, m_padded, n, k, s);
+      break;
+    default:
+      e = run_choice<EPI_SWIGLU>(ch, a, w, w2, c, nullptr, part, m, m_padded, n, k, s);
+      break;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || ch.splits == 1) return e;
+  const int mlim = epi == EPI_RESIDUAL ? m : m_padded;
+  const int threads = mlim * (n / 4);
+  if (threads == 0) return hipSuccess;
+  if (epi == EPI_RESIDUAL)
+    hipLaunchKernelGGL(gemm_splitk_reduce<EPI_RESIDUAL>, dim3((threads + 255) / 256), dim3(256), 0,
+                       s, part, ch.splits, c, residual, m, m_padded, n);
+  else
+    hipLaunchKernelGGL(gemm_splitk_reduce<EPI_STORE>, dim3((threads + 255) / 256), dim3(256), 0,
+                       s, part, ch.splits, c, residual, m, m_padded, n);
+  return hipGetLastError();
 }
 
 }  // namespace hl

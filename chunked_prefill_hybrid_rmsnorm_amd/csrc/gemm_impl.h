@@ -1,0 +1,230 @@
+// Tile template of the bf16 MFMA GEMM (see gemm.hip for the design notes).
+#pragma once
+#include "kernels.h"
+
+namespace hl {
+
+constexpr int kGemmBK = 64;
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// Global -> LDS copies (global_load_lds_dwordx4, no
+// register staging) into a ring of STAGES buffers, so STAGES-1 k-steps of
+// loads are in flight while one is multiplied.  BK = 64: one tile row is 128 B
+// = 8 chunks of 16 B; chunk c of row r sits in slot c ^ (r % 8), which keeps
+// the 16-row fragment reads free of bank conflicts.  One copy instruction
+// fills 1 KB = 8 rows; wave w issues blocks w, w + NW, ...  Rows past the end
+// of A or W are clamped to the last valid row: their products only reach
+// outputs that are never stored.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter: wait until at most n remain.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W2,
+    bf16* __restrict__ C, const bf16* __restrict__ R, float* __restrict__ part, int M, int Mp,
+    int N, int K, int n_mtiles, int n_ntiles, int splits) {
+  constexpr int BK = 64;
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  constexpr int A_BLK = BM / 8, W_BLK = BN / 8;  // 1 KB blocks per stage
+  constexpr int NBLK = A_BLK + W_BLK;
+  constexpr int PER_WAVE = NBLK / NW;             // copy instructions per wave per stage
+  constexpr int STAGE_BYTES = NBLK * 1024;
+  static_assert(BM % 8 == 0 && BN % 8 == 0 && NBLK % NW == 0, "blocks must split evenly over waves");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole MFMA blocks");
+  static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && (BN / 2) % 8 == 0), "swiglu pairing");
+  static_assert(STAGES >= 3, "need at least three stages");
+  static_assert(PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
+
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int total = n_mtiles * n_ntiles * splits;
+  const int b = blockIdx.x;
+  const int per = total / 8, rem = total % 8;
+  const int xcd = b % 8, slot = b / 8;
+  const int tile = xcd * per + min(xcd, rem) + slot;
+  const int tm = tile % n_mtiles;
+  const int rest = tile / n_mtiles;
+  const int z = rest % splits;
+  const int tn = rest / splits;
+  const int m0 = tm * BM, n0 = tn * OUT_N;
+
+  const int KT = K / BK;
+  const int kt_per = (KT + splits - 1) / splits;
+  const int kt0 = min(KT, z * kt_per);
+  const int kt1 = min(KT, kt0 + kt_per);
+  const int nk = kt1 - kt0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int l16 = lane & 15, q = lane >> 4;
+
+  // per-lane source row pointers of this wave's copy blocks (k offset added per stage)
+  const bf16* src[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int blk = wave + i * NW;
+    const int row = blk * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    const bf16* p;
+    if (blk < A_BLK) {
+      const int m = min(m0 + row, Mp - 1);
+      p = A + (size_t)m * K;
+    } else {
+      const int wr = row - BM;
+      const bf16* base = W;
+      int n;
+      if (EPI == EPI_SWIGLU) {
+        const bool up = wr >= BN / 2;
+        base = up ? W2 : W;
+        n = n0 + (up ? wr - BN / 2 : wr);
+      } else {
+        n = n0 + wr;
+      }
+      p = base + (size_t)min(n, N - 1) * K;
+    }
+    src[i] = p + chunk * 8;
+  }
+  auto issue = [&](int step) {  // copy k-step `step` (clamped) into its ring slot
+    const int kt = kt0 + min(step, max(nk - 1, 0));
+    char* st = smem + (step % STAGES) * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) lds_dma16(src[i] + kt * BK, st + (wave + i * NW) * 1024);
+  };
+
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment byte offsets inside a stage (row-dependent swizzle)
+  int a_off[FM], w_off[FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int row = wm * WTM + fm * 16 + l16;
+    a_off[fm] = row * 128;
+  }
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    int row;
+    if (EPI == EPI_SWIGLU) {
+      constexpr int HALF = FN / 2;
+      row = fn < HALF ? wn * (WTN / 2) + fn * 16 : BN / 2 + wn * (WTN / 2) + (fn - HALF) * 16;
+    } else {
+      row = wn * WTN + fn * 16;
+    }
+    row += l16;
+    w_off[fn] = (BM + row) * 128;
+  }
+  const int sw = l16 & 7;  // rows of a fragment are consecutive: row % 8 == l16 % 8 (+ const)
+
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(s);
+    for (int it = 0; it < nk; ++it) {
+      wait_vmcnt<PER_WAVE * (STAGES - 2)>();
+      asm volatile("" ::: "memory");  // keep LDS reads and copies on their side of the barrier
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(it + STAGES - 1);
+      const char* st = smem + (it % STAGES) * STAGE_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 af[FN], bfr[FM];
+        const int c = ks * 4 + q;
+        const int so = ((c ^ sw) << 4);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) af[fn] = as_bf16x8(ld16(st + w_off[fn] + so));
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) bfr[fm] = as_bf16x8(ld16(st + a_off[fm] + so));
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma16x16x32(af[fn], bfr[fm], acc[fn][fm]);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // drain the clamped tail copies before the workgroup ends
+
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = m0 + wm * WTM + fm * 16 + l16;
+    if (splits > 1) {
+      if (m >= Mp) continue;
+      float* pp = part + (size_t)z * Mp * N + (size_t)m * N;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + wn * WTN + fn * 16 + 4 * q;
+        if (n < N) *reinterpret_cast<f32x4*>(pp + n) = acc[fn][fm];
+      }
+      continue;
+    }
+    if (EPI == EPI_SWIGLU) {
+      if (m >= Mp) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN / 2; ++fn) {
+        const int n = n0 + wn * (WTN / 2) + fn * 16 + 4 * q;
+        if (n >= N) continue;
+        const f32x4 g = acc[fn][fm], u = acc[fn + FN / 2][fm];
+        u32x2 o;
+        o[0] = pack2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
+        o[1] = pack2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
+        *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
+      }
+    } else {
+      const int mlim = EPI == EPI_RESIDUAL ? M : Mp;
+      if (m >= mlim) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + wn * WTN + fn * 16 + 4 * q;
+        if (n >= N) continue;
+        f32x4 v = acc[fn][fm];
+        if (EPI == EPI_RESIDUAL) {
+          const u32x2 rr = ld8(R + (size_t)m * N + n);
+          v[0] += __uint_as_float(rr[0] << 16);
+          v[1] += __uint_as_float(rr[0] & 0xffff0000u);
+          v[2] += __uint_as_float(rr[1] << 16);
+          v[3] += __uint_as_float(rr[1] & 0xffff0000u);
+        }
+        u32x2 o;
+        o[0] = pack2(v[0], v[1]);
+        o[1] = pack2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES>
+hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, const bf16* r,
+                        float* part, int m, int mp, int n, int k, int splits, hipStream_t s) {
+  constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  constexpr size_t lds = (size_t)STAGES * (BM + BN) * 128;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  const int mt = (mp + BM - 1) / BM, nt = (n + OUT_N - 1) / OUT_N;
+  if (EPI == EPI_SWIGLU) splits = 1;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES>;
+  // raise the dynamic LDS limit once per instantiation (thread-safe static init)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(mt * nt * splits), dim3(64 * WM * WN), lds, s, a, w, w2, c, r, part,
+                     m, mp, n, k, mt, nt, splits);
+  return hipGetLastError();
+}
+
+}  // namespace hl

@@ -20,17 +20,23 @@ hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* y, int rows, int r
                           int hidden, float eps, hipStream_t s);
 
 enum GemmEpilogue { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
-// c = a w^T (+ residual) / swiglu(a w_gate^T, a w_up^T).
+// c = a w^T (+ residual) / swiglu(a w_gate^T, a w_up^T).  ws holds split-K
+// partials (gemm_workspace_bytes); with ws == nullptr K is not split.
+size_t gemm_workspace_bytes(GemmEpilogue epi, int m_padded, int n, int k);
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
-                       const bf16* residual, int m, int m_padded, int n, int k, hipStream_t s);
+                       const bf16* residual, void* ws, int m, int m_padded, int n, int k,
+                       hipStream_t s);
 
 hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* slot, int rows,
                                  int nq, int nkv, int d, float theta, const KvDev& kv,
                                  hipStream_t s);
 
+// ws (prefill_workspace_bytes) holds key-split partials; nullptr: no split.
+size_t prefill_workspace_bytes(const ChunkList& chunks, int nq, int nkv, int d);
+size_t prefill_workspace_bound(int rows, int nq, int nkv, int d);
 hipError_t launch_prefill_attention(const bf16* qkv, int nq, int nkv, int d,
                                     const ChunkList& chunks, const KvDev& kv, bf16* attn,
-                                    hipStream_t s);
+                                    void* ws, hipStream_t s);
 
 size_t decode_workspace_bytes(int n_decodes, int nq, int d, int max_ctx);
 hipError_t launch_decode_attention(const bf16* qkv, int row0, int nq, int nkv, int d,

@@ -173,9 +173,14 @@ int hl_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
 /* c[m, n] = sum_k a[m, k] w[n, k] (+ residual[m, n]) in fp32, rounded to bf16.
  * a [m_padded, k], w [n, k], c and residual [*, n] row-major.  Without a
  * residual all m_padded rows are written; with one only the first m rows.
- * k multiple of 64, n multiple of 64, m_padded multiple of 16. */
+ * k multiple of 64, n multiple of 64, m_padded multiple of 16.  ws (device,
+ * 16-byte aligned, ws_bytes >= hl_gemm_workspace_bytes) lets the kernel split
+ * K over more workgroups; with ws == NULL K is not split (same results up to
+ * fp32 summation order). */
 int hl_gemm_bf16(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
-                 int32_t m, int32_t m_padded, int32_t n, int32_t k, hipStream_t stream);
+                 int32_t m, int32_t m_padded, int32_t n, int32_t k, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+int hl_gemm_workspace_bytes(int32_t m_padded, int32_t n, int32_t k, size_t* bytes);
 
 /* act[m, f] = silu(sum_k a[m,k] w_gate[f,k]) * sum_k a[m,k] w_up[f,k] for
  * m < m_padded; silu(z) = z / (1 + exp(-z)).  a [m_padded, k],
@@ -193,9 +198,14 @@ int hl_rope_kv_append(const hl_config* cfg, hl_bf16* qkv, const int32_t* positio
 /* Chunk-prefill attention.  Chunk c's rows start at row sum_{i<c} len_i of
  * qkv (q already rotated, its own K/V already appended); row i of the chunk
  * (position start_pos + i) attends keys 0 .. start_pos + i through the
- * chunk's block table.  Writes attn rows of the chunks ([*, nq d]). */
+ * chunk's block table.  Writes attn rows of the chunks ([*, nq d]).  ws
+ * (device, 16-byte aligned, >= hl_prefill_workspace_bytes) lets the kernel
+ * split long key ranges over more workgroups; ws == NULL: no split. */
 int hl_prefill_attention(const hl_config* cfg, const hl_bf16* qkv, const hl_chunk* chunks,
-                         int32_t n_chunks, const hl_kv* kv, hl_bf16* attn, hipStream_t stream);
+                         int32_t n_chunks, const hl_kv* kv, hl_bf16* attn, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+int hl_prefill_workspace_bytes(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,
+                               size_t* bytes);
 
 /* Paged decode attention, split-K over 256-key partitions plus a merge.
  * Decode j reads its q from qkv row row0 + j and writes attn row row0 + j.

@@ -128,6 +128,9 @@ EDGE = {
     "two_chunks": dict(chunk_lens=[20, 45], chunk_starts=[0, 70], n_decodes=3),
     "three_chunks_ragged": dict(chunk_lens=[3, 17, 29], chunk_starts=[5, 0, 33], n_decodes=2),
     "long_decode_multi_partition": dict(chunk_lens=[8], chunk_starts=[0], ctx_lens=[255, 256, 700, 1300]),
+    # few chunk rows after a long prefix: the key range is split over workgroups and merged
+    "long_prior_chunk_key_split": dict(chunk_lens=[40], chunk_starts=[1000], n_decodes=2),
+    "two_long_chunks_key_split": dict(chunk_lens=[33, 7], chunk_starts=[700, 1500], ctx_lens=[31, 32]),
 }
 
 
