@@ -58,58 +58,6 @@ def make_batch(name):
     return I.tiny_batch(seed=0), "tiny layer H=256: Lp=64 (64 cached) + Bd=4 decodes, ctx U[16,128]"
 
 
-def stage_runners(db, copies, B):
-    """One launcher per kernel, same arguments as inside hl_layer_forward,
-    fed from the rotated copies.  Returns {stage name: fn(i)}."""
-    import torch
-    s = db.shape
-    M, Mp = db.M, db.Mp
-    H, F, nq, nkv, d = s.hidden, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim
-    nqkv = s.qkv_rows
-    dev = db.x.device
-    e = lambda n: torch.empty((Mp, n), dtype=torch.bfloat16, device=dev)
-    xn, qkv, attn, h, act = e(H), e(nqkv), e(nq * d), e(H), e(F)
-    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-    pos = torch.empty(M, dtype=torch.int32, device=dev)
-    slot = torch.empty(M, dtype=torch.int32, device=dev)
-    B.hl_slot_mapping(db.cfg, db.chunks, db.dec, db.kv.num_pages, pos, slot)
-    dws = B.hl_decode_workspace_bytes(db.cfg, db.dec.n, db.dec.max_ctx) if db.dec.n else 0
-    dws_t = torch.empty(max(dws, 256), dtype=torch.uint8, device=dev)
-    pws = B.hl_prefill_workspace_bytes(db.cfg, db.chunks)
-    pws_t = torch.empty(max(pws, 256), dtype=torch.uint8, device=dev)
-    gws = max(B.hl_gemm_workspace_bytes(Mp, n_, k_) for n_, k_ in
-              ((nqkv, H), (H, nq * d), (H, F)))
-    gws_t = torch.empty(max(gws, 256), dtype=torch.uint8, device=dev)
-    x = db.x
-    # fill the activations once so every stage reads realistic values
-    w0, kv0 = copies[0]
-    B.hl_rmsnorm(x, w0[0]["g_attn"], xn, M, Mp, H, s.rms_eps)
-    B.hl_gemm_bf16(xn, w0[0]["w_qkv"], qkv, None, M, Mp, nqkv, H)
-    torch.cuda.synchronize()
-    lp = sum(c.length for c in db.hb.chunks)
-
-    def W(i):
-        return copies[i % len(copies)][0][0]
-
-    def KV(i):
-        return copies[i % len(copies)][1]
-
-    return {
-        "rmsnorm1": lambda i: B.hl_rmsnorm(x, W(i)["g_attn"], xn, M, Mp, H, s.rms_eps),
-        "gemm_qkv": lambda i: B.hl_gemm_bf16(xn, W(i)["w_qkv"], qkv, None, M, Mp, nqkv, H,
-                                             gws_t, gws),
-        "rope_kv_append": lambda i: B.hl_rope_kv_append(db.cfg, qkv, pos, slot, M, KV(i)),
-        "prefill_attn": lambda i: B.hl_prefill_attention(db.cfg, qkv, db.chunks, KV(i), attn,
-                                                         pws_t, pws),
-        "decode_attn": lambda i: B.hl_decode_attention(db.cfg, qkv, lp, db.dec, KV(i), attn,
-                                                       dws_t, dws),
-        "gemm_o": lambda i: B.hl_gemm_bf16(attn, W(i)["w_o"], h, x, M, Mp, H, nq * d, gws_t, gws),
-        "rmsnorm2": lambda i: B.hl_rmsnorm(h, W(i)["g_ffn"], xn, M, Mp, H, s.rms_eps),
-        "gemm_gate_up": lambda i: B.hl_gemm_swiglu(xn, W(i)["w_gate"], W(i)["w_up"], act, Mp, F, H),
-        "gemm_down": lambda i: B.hl_gemm_bf16(act, W(i)["w_down"], out, h, M, Mp, H, F, gws_t, gws),
-    }
-
-
 def time_loop(fn, steps, warmup):
     """Average ms per call, HIP events on the current stream (the one the
     library launches on)."""
@@ -191,31 +139,47 @@ def main():
     tok_s = M / (ms / 1e3)
     log(f"layer {ms * 1e3:.1f} us/step, {tok_s / 1e6:.3f} M tokens/s")
 
-    # per-kernel times (same kernels, same arguments, rotated weights/KV)
-    runners = stage_runners(db, copies, B)
+    # per-step times inside the real layer sequence: HIP events recorded by the
+    # library between its steps, on the stream it launches on
+    log("per-step timing with stage events ...")
+    names = B.stage_names()
+    ns = len(names)
+
+    def make_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)]
+        for e in evs:  # materialise the underlying HIP events
+            e.record()
+        return evs
+
+    ev_sets = [make_events() for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    for i in range(a.warmup):
+        layer(i)
+    for i in range(a.steps):
+        (wt, ws), kv = copies[i % len(copies)]
+        B.hl_layer_forward_timed(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws,
+                                 db.ws_bytes, a.pad, ev_sets[i])
+    torch.cuda.synchronize()
     lens = [c.length for c in hb.chunks]
     starts = [c.start_pos for c in hb.chunks]
     stages = {s.name: s for s in RL.layer_stages(hb.shape.hidden, hb.shape.n_q_heads,
                                                   hb.shape.n_kv_heads, hb.shape.head_dim,
                                                   hb.shape.ffn, lens, starts,
                                                   [int(c) for c in hb.decodes.ctx_lens], a.pad)}
-    for i, fn in enumerate(runners.values()):  # fill every buffer once, in layer order
-        fn(0)
-    torch.cuda.synchronize()
     table = {}
-    for name, fn in runners.items():
-        t = time_loop(fn, a.steps, a.warmup) * 1e-3
+    for k, name in enumerate(names):
+        t = sum(ev[k].elapsed_time(ev[k + 1]) for ev in ev_sets) / a.steps * 1e-3
         st = stages[name]
         table[name] = {
             "us": round(t * 1e6, 2),
             "bound": st.bound,
             "t_roof_us": round(st.t_roof() * 1e6, 2),
-            "roof_frac": round(st.t_roof() / t, 4),
-            "GB/s": round(st.bytes / t / 1e9, 1),
-            "TFLOP/s": round(st.flops / t / 1e12, 2),
+            "roof_frac": round(st.t_roof() / t, 4) if t > 0 else None,
+            "GB/s": round(st.bytes / t / 1e9, 1) if t > 0 else None,
+            "TFLOP/s": round(st.flops / t / 1e12, 2) if t > 0 else None,
         }
-        log(f"  {name:15s} {t * 1e6:8.1f} us  roof {st.t_roof() * 1e6:7.1f} us  "
-            f"({st.bound}, frac {st.t_roof() / t:.3f})")
+        log(f"  {name:16s} {t * 1e6:8.1f} us  roof {st.t_roof() * 1e6:7.1f} us  "
+            f"({st.bound}, frac {table[name]['roof_frac']})")
     dom = max(table, key=lambda k: table[k]["us"])
     st = stages[dom]
     t_dom = table[dom]["us"] * 1e-6

@@ -73,6 +73,11 @@ _SIGS = {
                                     _c.c_int32, _P(hl_decodes), _P(hl_kv), _c.c_void_p,
                                     _c.c_void_p, _c.c_size_t, _c.c_int32, _P(hl_taps),
                                     _c.c_void_p]),
+    "hl_layer_forward_timed": (_c.c_int, [_P(hl_config), _P(hl_weights), _c.c_void_p,
+                                          _P(hl_chunk), _c.c_int32, _P(hl_decodes), _P(hl_kv),
+                                          _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int32,
+                                          _P(hl_taps), _P(_c.c_void_p), _c.c_void_p]),
+    "hl_stage_name": (_c.c_char_p, [_c.c_int]),
     "hl_slot_mapping": (_c.c_int, [_P(hl_config), _P(hl_chunk), _c.c_int32, _P(hl_decodes),
                                    _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "hl_validate_metadata": (_c.c_int, [_P(hl_config), _P(hl_chunk), _c.c_int32,
@@ -112,6 +117,10 @@ def load(path: Optional[str] = None):
     if not os.path.exists(p):
         raise RuntimeError(f"HIP library not built: {p} is missing "
                            "(run python -m chunked_prefill_hybrid_rmsnorm_amd.build)")
+    try:  # share torch's HIP runtime (streams and events cross the ABI)
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover
+        pass
     lib = ctypes.CDLL(p)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
@@ -211,6 +220,26 @@ def hl_layer_forward(cfg, weights: hl_weights, x, chunks: Sequence[hl_chunk], de
                                  ws_bytes, pad, ctypes.byref(taps) if taps is not None else None,
                                  _stream(stream))
     _check(rc, "hl_layer_forward")
+
+
+N_STAGES = 7
+
+
+def stage_names():
+    return [load().hl_stage_name(i).decode() for i in range(N_STAGES)]
+
+
+def hl_layer_forward_timed(cfg, weights: hl_weights, x, chunks, dec: hl_decodes, kv: hl_kv, out,
+                           ws, ws_bytes: int, pad: int, events, taps=None, stream=None):
+    """``events``: N_STAGES + 1 torch.cuda.Event objects (timing enabled)."""
+    arr, n = _chunk_array(chunks)
+    handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    rc = load().hl_layer_forward_timed(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x), arr, n,
+                                       ctypes.byref(dec), ctypes.byref(kv), _ptr(out), _ptr(ws),
+                                       ws_bytes, pad,
+                                       ctypes.byref(taps) if taps is not None else None, handles,
+                                       _stream(stream))
+    _check(rc, "hl_layer_forward_timed")
 
 
 def hl_slot_mapping(cfg, chunks, dec, num_pages, positions, slots, stream=None):

@@ -32,6 +32,9 @@ def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
             # packed fp32 VALU ops stay off: the compiler must not form them
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in ordinary VGPRs: with accumulators split
+            # across VGPR/AGPR the compiler shuffles them every k-step
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-result"]
 
 

@@ -129,10 +129,19 @@ int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t m
   return HL_OK;
 }
 
-int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
-                     const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
-                     const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
-                     const hl_taps* taps, hipStream_t stream) {
+static const char* const kStageNames[HL_N_STAGES] = {
+    "rmsnorm1", "gemm_qkv", "rope_kv_append", "attention", "gemm_o_rmsnorm2", "gemm_gate_up",
+    "gemm_down"};
+
+const char* hl_stage_name(int stage) {
+  return (stage >= 0 && stage < HL_N_STAGES) ? kStageNames[stage] : "";
+}
+
+static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                              const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                              const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes,
+                              int32_t pad, const hl_taps* taps, hipStream_t stream,
+                              hipEvent_t* ev) {
   int e = check_config(cfg);
   if (e) return e;
   if (!w || !x || !kv || !out || !ws || !kv->data) return HL_ERR_NULL;
@@ -156,8 +165,6 @@ int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x
   };
   const hl_taps none{};
   const hl_taps& t = taps ? *taps : none;
-  int32_t* pos = reinterpret_cast<int32_t*>(base + L.pos);
-  int32_t* slot = reinterpret_cast<int32_t*>(base + L.slot);
   bf16* xn1 = pick(t.xn1, L.xn1);
   bf16* qkv = pick(t.qkv, L.qkv);
   bf16* attn = pick(t.attn, L.attn);
@@ -176,36 +183,70 @@ int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x
   do {                                    \
     if ((r = (call)) != hipSuccess) return HL_ERR_LAUNCH; \
   } while (0)
-  // a0: positions and slots of every row
-  HL_TRY(launch_slot_map(cl, dd, cfg->page_size, kv->num_pages, pos, slot, stream));
+  int stage = 0;
+  auto mark = [&]() {
+    if (ev && hipEventRecord(ev[stage], stream) != hipSuccess) return false;
+    ++stage;
+    return true;
+  };
+#define HL_MARK() \
+  do {            \
+    if (!mark()) return HL_ERR_HIP; \
+  } while (0)
+  HL_MARK();
   // a1: RMSNorm (pad rows -> 0)
   HL_TRY(launch_rmsnorm(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
                         cfg->rms_eps, stream));
+  HL_MARK();
   // a2: fused QKV projection on the stacked rows
   void* gws = base + L.gemm;
   HL_TRY(launch_gemm(EPI_STORE, xn1, reinterpret_cast<const bf16*>(w->w_qkv), nullptr, qkv,
                      nullptr, gws, M, Mp, nqkv, H, stream));
-  // a3: RoPE on q and k, append K and V of every row into its page
-  HL_TRY(launch_rope_kv_append(qkv, pos, slot, M, nq, nkv, d, cfg->rope_theta, kvd, stream));
-  // a4: chunk-prefill attention on rows [0, Lp)
-  HL_TRY(launch_prefill_attention(qkv, nq, nkv, d, cl, kvd, attn, base + L.pre, stream));
-  // a5: paged decode attention on rows [Lp, M)
-  HL_TRY(launch_decode_attention(qkv, cl.n_rows, nq, nkv, d, dd, kvd, attn, base + L.dec, stream));
-  // a6: O projection + residual
-  HL_TRY(launch_gemm(EPI_RESIDUAL, attn, reinterpret_cast<const bf16*>(w->w_o), nullptr, h, xin,
-                     gws, M, Mp, H, nq * d, stream));
-  // a7: RMSNorm
-  HL_TRY(launch_rmsnorm(h, reinterpret_cast<const bf16*>(w->g_ffn), xn2, M, Mp, H, cfg->rms_eps,
-                        stream));
+  HL_MARK();
+  // a0 + a3: each row's position and KV slot, RoPE on q and k, append K and V
+  HL_TRY(launch_rope_kv_append_meta(qkv, cl, dd, nq, nkv, d, cfg->rope_theta, kvd, stream));
+  HL_MARK();
+  // a4 + a5: chunk-prefill attention (rows [0, Lp)) and paged decode attention
+  // (rows [Lp, M)) in one launch
+  HL_TRY(launch_attention(qkv, nq, nkv, d, cl, dd, cl.n_rows, kvd, attn, base + L.pre,
+                          base + L.dec, stream));
+  HL_MARK();
+  // a6 + a7: O projection + residual, then RMSNorm (fused into the split-K reduce)
+  HL_TRY(launch_gemm_residual_norm(attn, reinterpret_cast<const bf16*>(w->w_o), h, xin,
+                                   reinterpret_cast<const bf16*>(w->g_ffn), xn2, cfg->rms_eps, gws,
+                                   M, Mp, H, nq * d, stream));
+  HL_MARK();
   // a8: gate/up projection + SwiGLU
   HL_TRY(launch_gemm(EPI_SWIGLU, xn2, reinterpret_cast<const bf16*>(w->w_gate),
                      reinterpret_cast<const bf16*>(w->w_up), act, nullptr, nullptr, M, Mp, F, H,
                      stream));
+  HL_MARK();
   // a9: down projection + residual
   HL_TRY(launch_gemm(EPI_RESIDUAL, act, reinterpret_cast<const bf16*>(w->w_down), nullptr,
                      reinterpret_cast<bf16*>(out), h, gws, M, Mp, H, F, stream));
+  HL_MARK();
+#undef HL_MARK
 #undef HL_TRY
   return HL_OK;
+}
+
+int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                     const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                     const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
+                     const hl_taps* taps, hipStream_t stream) {
+  return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws, ws_bytes, pad, taps,
+                            stream, nullptr);
+}
+
+int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                           const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                           const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
+                           const hl_taps* taps, hipEvent_t* stage_events, hipStream_t stream) {
+  if (!stage_events) return HL_ERR_NULL;
+  for (int i = 0; i <= HL_N_STAGES; ++i)
+    if (!stage_events[i]) return HL_ERR_NULL;
+  return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws, ws_bytes, pad, taps,
+                            stream, stage_events);
 }
 
 int hl_slot_mapping(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,

@@ -7,9 +7,9 @@
 //   O^T[dim][row] += V^T[dim][key] P^T[key][row]   A = V^T (dim-major page)
 // Lane l holds row l % 16 of every tile, so the probabilities it computes
 // are exactly the B operand it feeds to the second product.  Softmax is
-// online in base 2.  Keys are visited 32 at a time (two pages); the next
-// step's page ids and K/V fragments are loaded while the current step is
-// multiplied, so a step costs one exposed memory latency at most once.
+// online in base 2.  Keys are visited 32 at a time (two pages); page ids come
+// from a register window of the block table and the next step's K/V
+// fragments are loaded while the current step is multiplied.
 #pragma once
 #include "kernels.h"
 
@@ -28,15 +28,6 @@ struct KvFrag {
   u32x4 k[2][D / 32];  // two pages, K rows (16 B per lane per k-step)
   u32x2 v[2][D / 16];  // two pages, V^T pieces (8 B per lane per dim block)
 };
-
-__device__ __forceinline__ int page_of(const int32_t* bt, int n_blocks, int t, int kv_len,
-                                       int num_pages) {
-  if (t >= kv_len) return -1;
-  const int blk = t >> 4;
-  if (blk >= n_blocks) return -1;
-  const int pg = bt[blk];
-  return (pg >= 0 && pg < num_pages) ? pg : -1;
-}
 
 template <int D>
 __device__ __forceinline__ void load_step(KvFrag<D>& f, const KvDev& kv, int g, int p0, int p1,
@@ -116,6 +107,30 @@ __device__ __forceinline__ void compute_step(AttnAcc<D>& a, const KvFrag<D>& f,
   }
 }
 
+// A wave's window of 64 consecutive block-table entries (lane i holds the page
+// of block base + i, or -1 past the table, the segment or the pool), so that
+// a step's page ids are a register read instead of a dependent global load.
+struct PageWindow {
+  int base = -(1 << 30);
+  int page = -1;
+  __device__ __forceinline__ void fill(const int32_t* bt, int n_blocks, int blk0, int blk_end,
+                                       int num_pages, int lane) {
+    base = blk0;
+    const int b = blk0 + lane;
+    int pg = -1;
+    if (b < n_blocks && b < blk_end) pg = bt[b];
+    page = (pg >= 0 && pg < num_pages) ? pg : -1;
+  }
+  // page of key t (uniform across the wave), refilling the window when needed
+  __device__ __forceinline__ int at(int t, const int32_t* bt, int n_blocks, int blk_end,
+                                    int num_pages, int lane) {
+    const int b = t >> 4;
+    if (b >= blk_end) return -1;
+    if (b - base >= 64 || b < base) fill(bt, n_blocks, b, blk_end, num_pages, lane);
+    return __builtin_amdgcn_readlane(page, b - base);
+  }
+};
+
 // Keys [k0, k1) (k0 a multiple of 32) of one request through its block table.
 template <int D>
 __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)[D / 32],
@@ -124,22 +139,33 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
                                                int g, int l16, int q) {
   const float scale = kAttnLog2e * rsqrtf((float)D);
   if (k0 >= k1) return;
+  const int lane = l16 + 16 * q;
+  const int blk_end = (k1 + 15) >> 4;
+  PageWindow win;
+  win.fill(bt, n_blocks, k0 >> 4, blk_end, kv.num_pages, lane);
+  auto pages = [&](int t, int& p0, int& p1) {
+    p0 = win.at(t, bt, n_blocks, blk_end, kv.num_pages, lane);
+    p1 = win.at(t + 16, bt, n_blocks, blk_end, kv.num_pages, lane);
+  };
   KvFrag<D> fa, fb;
-  load_step<D>(fa, kv, g, page_of(bt, n_blocks, k0, k1, kv.num_pages),
-               page_of(bt, n_blocks, k0 + 16, k1, kv.num_pages), l16, q);
+  int p0, p1;
+  pages(k0, p0, p1);
+  load_step<D>(fa, kv, g, p0, p1, l16, q);
   int t0 = k0;
   while (true) {
     // fa holds step t0; fetch t0 + 32 into fb, then multiply fa
     const int t1 = t0 + 32;
-    if (t1 < k1)
-      load_step<D>(fb, kv, g, page_of(bt, n_blocks, t1, k1, kv.num_pages),
-                   page_of(bt, n_blocks, t1 + 16, k1, kv.num_pages), l16, q);
+    if (t1 < k1) {
+      pages(t1, p0, p1);
+      load_step<D>(fb, kv, g, p0, p1, l16, q);
+    }
     compute_step<D>(a, fa, qf, t0, row_limit, k1, kv_len, scale, q);
     if (t1 >= k1) break;
     const int t2 = t1 + 32;
-    if (t2 < k1)
-      load_step<D>(fa, kv, g, page_of(bt, n_blocks, t2, k1, kv.num_pages),
-                   page_of(bt, n_blocks, t2 + 16, k1, kv.num_pages), l16, q);
+    if (t2 < k1) {
+      pages(t2, p0, p1);
+      load_step<D>(fa, kv, g, p0, p1, l16, q);
+    }
     compute_step<D>(a, fb, qf, t1, row_limit, k1, kv_len, scale, q);
     if (t2 >= k1) break;
     t0 = t2;

@@ -52,6 +52,71 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(const float* __restric
   *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
 }
 
+// Split-K reduce of a residual GEMM fused with the RMSNorm that follows it:
+// one 256-thread workgroup per row sums the partials (8 columns per thread
+// per pass), adds the residual, stores h (bf16) and y = h / sqrt(mean(h^2) +
+// eps) * g computed from that stored h.  Rows in [M, Mp) get y = 0 (dummy
+// tokens).  N = hidden, a multiple of 64, at most 256 * 8 * CH.
+template <int CH>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_norm(
+    const float* __restrict__ part, int splits, bf16* __restrict__ H_out,
+    const bf16* __restrict__ R, const bf16* __restrict__ g, bf16* __restrict__ Y, int M, int Mp,
+    int N, float eps) {
+  const int tid = threadIdx.x;
+  const int m = blockIdx.x;
+  bf16* yr = Y + (size_t)m * N;
+  if (m >= M) {
+    for (int c = tid * 8; c < N; c += 256 * 8) *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
+    return;
+  }
+  const size_t plane = (size_t)Mp * N;
+  u32x4 hv[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = (i * 256 + tid) * 8;
+    if (c >= N) {
+      hv[i] = u32x4{0, 0, 0, 0};
+      continue;
+    }
+    const float* p = part + (size_t)m * N + c;
+    f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    for (int z = 1; z < splits; ++z) {
+      a += *reinterpret_cast<const f32x4*>(p + z * plane);
+      b += *reinterpret_cast<const f32x4*>(p + z * plane + 4);
+    }
+    const u32x4 rr = ld16(R + (size_t)m * N + c);
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hv[i][e] = pack2(v[2 * e] + __uint_as_float(rr[e] << 16),
+                       v[2 * e + 1] + __uint_as_float(rr[e] & 0xffff0000u));
+      const float h0 = __uint_as_float(hv[i][e] << 16), h1 = __uint_as_float(hv[i][e] & 0xffff0000u);
+      ss += h0 * h0 + h1 * h1;
+    }
+    *reinterpret_cast<u32x4*>(H_out + (size_t)m * N + c) = hv[i];
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = (i * 256 + tid) * 8;
+    if (c >= N) continue;
+    const u32x4 gv = ld16(g + c);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = __uint_as_float(hv[i][e] << 16) * inv * __uint_as_float(gv[e] << 16);
+      const float b = __uint_as_float(hv[i][e] & 0xffff0000u) * inv * __uint_as_float(gv[e] & 0xffff0000u);
+      o[e] = pack2(a, b);
+    }
+    *reinterpret_cast<u32x4*>(yr + c) = o;
+  }
+}
+
 // ------------------------------------------------------------ dispatch
 // Row tile: 288 rows (one tile spans a whole hybrid batch of up to 288 rows,
 // so every weight tile is streamed from HBM once) or 128 rows for small
@@ -118,6 +183,34 @@ hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf1
   else
     hipLaunchKernelGGL(gemm_splitk_reduce<EPI_STORE>, dim3((threads + 255) / 256), dim3(256), 0,
                        s, part, ch.splits, c, residual, m, m_padded, n);
+  return hipGetLastError();
+}
+
+template <int CH>
+static void launch_rn(const float* part, int splits, bf16* h, const bf16* r, const bf16* g,
+                      bf16* y, int m, int mp, int n, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_splitk_reduce_norm<CH>, dim3(mp), dim3(256), 0, s, part, splits, h, r, g,
+                     y, m, mp, n, eps);
+}
+
+hipError_t launch_gemm_residual_norm(const bf16* a, const bf16* w, bf16* h, const bf16* residual,
+                                     const bf16* g, bf16* y, float eps, void* ws, int m,
+                                     int m_padded, int n, int k, hipStream_t s) {
+  if (m_padded == 0 || n == 0) return hipSuccess;
+  Choice ch = choose(EPI_RESIDUAL, m_padded, n, k);
+  const int nch = (n + 2047) / 2048;  // 8-column chunks per thread
+  if (ch.splits == 1 || ws == nullptr || nch > 8) {
+    hipError_t e = launch_gemm(EPI_RESIDUAL, a, w, nullptr, h, residual, ws, m, m_padded, n, k, s);
+    if (e != hipSuccess) return e;
+    return launch_rmsnorm(h, g, y, m, m_padded, n, eps, s);
+  }
+  float* part = reinterpret_cast<float*>(ws);
+  hipError_t e = run_choice<EPI_RESIDUAL>(ch, a, w, nullptr, h, residual, part, m, m_padded, n, k, s);
+  if (e != hipSuccess) return e;
+  if (nch <= 1) launch_rn<1>(part, ch.splits, h, residual, g, y, m, m_padded, n, eps, s);
+  else if (nch <= 2) launch_rn<2>(part, ch.splits, h, residual, g, y, m, m_padded, n, eps, s);
+  else if (nch <= 4) launch_rn<4>(part, ch.splits, h, residual, g, y, m, m_padded, n, eps, s);
+  else launch_rn<8>(part, ch.splits, h, residual, g, y, m, m_padded, n, eps, s);
   return hipGetLastError();
 }
 

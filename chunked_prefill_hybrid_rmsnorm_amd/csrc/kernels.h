@@ -27,9 +27,19 @@ hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf1
                        const bf16* residual, void* ws, int m, int m_padded, int n, int k,
                        hipStream_t s);
 
+// h = a w^T + residual (rows < m) followed by y = RMSNorm(h; g, eps) (rows
+// < m_padded, pad rows zero); with split K the norm runs inside the reduce.
+hipError_t launch_gemm_residual_norm(const bf16* a, const bf16* w, bf16* h, const bf16* residual,
+                                     const bf16* g, bf16* y, float eps, void* ws, int m,
+                                     int m_padded, int n, int k, hipStream_t s);
+
 hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* slot, int rows,
                                  int nq, int nkv, int d, float theta, const KvDev& kv,
                                  hipStream_t s);
+// same, with each row's position and slot taken from the batch metadata
+hipError_t launch_rope_kv_append_meta(bf16* qkv, const ChunkList& chunks, const DecDev& dec,
+                                      int nq, int nkv, int d, float theta, const KvDev& kv,
+                                      hipStream_t s);
 
 // ws (prefill_workspace_bytes) holds key-split partials; nullptr: no split.
 size_t prefill_workspace_bytes(const ChunkList& chunks, int nq, int nkv, int d);
@@ -39,6 +49,11 @@ hipError_t launch_prefill_attention(const bf16* qkv, int nq, int nkv, int d,
                                     void* ws, hipStream_t s);
 
 size_t decode_workspace_bytes(int n_decodes, int nq, int d, int max_ctx);
+// Prefill rows and decode rows in one launch (plus one merge when keys were
+// split); pf_ws / dc_ws as for the two launchers below.
+hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const ChunkList& chunks,
+                            const DecDev& dec, int dec_row0, const KvDev& kv, bf16* attn,
+                            void* pf_ws, void* dc_ws, hipStream_t s);
 hipError_t launch_decode_attention(const bf16* qkv, int row0, int nq, int nkv, int d,
                                    const DecDev& dec, const KvDev& kv, bf16* attn, void* ws,
                                    hipStream_t s);

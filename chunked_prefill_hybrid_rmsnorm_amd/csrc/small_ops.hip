@@ -1,5 +1,7 @@
 // Row metadata, RMSNorm and RoPE + KV append: the HBM-bound small steps of
 // the hybrid-batch layer.
+#include <string.h>
+
 #include "kernels.h"
 
 namespace hl {
@@ -7,12 +9,11 @@ namespace hl {
 // ----------------------------------------------------------------- slots
 // Row r < n_rows of the chunks: position start_pos + (r - row0) of its chunk;
 // decode row j: position ctx_lens[j].  Slot = page * page_size + offset with
-// page = block_table[pos / page_size] (PagedAttention addressing).
-__global__ void slot_map_kernel(ChunkList chunks, DecDev dec, int page_size, int num_pages,
-                                int32_t* __restrict__ pos_out, int32_t* __restrict__ slot_out) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  const int total = chunks.n_rows + dec.n;
-  if (r >= total) return;
+// page = block_table[pos / page_size] (PagedAttention addressing); -1 when the
+// table or the page id is out of range.
+__device__ __forceinline__ void row_pos_slot(const ChunkList& chunks, const DecDev& dec,
+                                             int page_size, int num_pages, int r, int* pos_out,
+                                             int* slot_out) {
   int pos, blk, page = -1;
   if (r < chunks.n_rows) {
     int c = 0;
@@ -26,8 +27,18 @@ __global__ void slot_map_kernel(ChunkList chunks, DecDev dec, int page_size, int
     blk = pos / page_size;
     if (blk >= 0 && blk < dec.max_blocks) page = dec.block_tables[(size_t)j * dec.max_blocks + blk];
   }
+  *pos_out = pos;
+  *slot_out = (page >= 0 && page < num_pages) ? page * page_size + pos % page_size : -1;
+}
+
+__global__ void slot_map_kernel(ChunkList chunks, DecDev dec, int page_size, int num_pages,
+                                int32_t* __restrict__ pos_out, int32_t* __restrict__ slot_out) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= chunks.n_rows + dec.n) return;
+  int pos, slot;
+  row_pos_slot(chunks, dec, page_size, num_pages, r, &pos, &slot);
   pos_out[r] = pos;
-  slot_out[r] = (page >= 0 && page < num_pages) ? page * page_size + pos % page_size : -1;
+  slot_out[r] = slot;
 }
 
 hipError_t launch_slot_map(const ChunkList& chunks, const DecDev& dec, int page_size,
@@ -40,91 +51,147 @@ hipError_t launch_slot_map(const ChunkList& chunks, const DecDev& dec, int page_
 }
 
 // ----------------------------------------------------------------- RMSNorm
-// One 256-thread block per row; 8 bf16 per thread per step (16-byte loads).
-constexpr int kNormThreads = 256;
+// One wave per row, four rows per workgroup; the row stays in registers
+// between the sum of squares and the scaling (one global read).  hidden is a
+// multiple of 64 and at most 64 * 8 * kNormMaxChunks.
+constexpr int kNormRowsPerBlock = 4;
+constexpr int kNormMaxChunks = 32;  // 16-byte chunks per lane: hidden <= 16384
 
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
-    const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
-    int hidden, float eps) {
-  const int r = blockIdx.x;
-  bf16* yr = y + (size_t)r * hidden;
-  const int tid = threadIdx.x;
-  if (r >= rows) {  // padding row: zero dummy token
-    for (int c = tid * 8; c < hidden; c += kNormThreads * 8)
-      *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
-    return;
-  }
-  const bf16* xr = x + (size_t)r * hidden;
+template <int CH>
+__device__ __forceinline__ void rmsnorm_row(const bf16* __restrict__ xr, const bf16* __restrict__ g,
+                                            bf16* __restrict__ yr, int hidden, float eps, int lane) {
+  u32x4 v[CH];
   float ss = 0.f;
-  for (int c = tid * 8; c < hidden; c += kNormThreads * 8) {
-    u32x4 v = ld16(xr + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = __uint_as_float(v[i] << 16), b = __uint_as_float(v[i] & 0xffff0000u);
+  for (int i = 0; i < CH; ++i) {
+    const int c = (i * 64 + lane) * 8;
+    v[i] = c < hidden ? ld16(xr + c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = __uint_as_float(v[i][e] << 16), b = __uint_as_float(v[i][e] & 0xffff0000u);
       ss += a * a + b * b;
     }
   }
-  __shared__ float part[kNormThreads / kWave];
   ss = wave_sum(ss);
-  if ((tid & 63) == 0) part[tid >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
+  const float inv = rsqrtf(ss / (float)hidden + eps);
 #pragma unroll
-  for (int i = 0; i < kNormThreads / kWave; ++i) tot += part[i];
-  const float inv = rsqrtf(tot / (float)hidden + eps);
-  for (int c = tid * 8; c < hidden; c += kNormThreads * 8) {
-    u32x4 v = ld16(xr + c), gv = ld16(g + c), o;
+  for (int i = 0; i < CH; ++i) {
+    const int c = (i * 64 + lane) * 8;
+    if (c >= hidden) continue;
+    const u32x4 gv = ld16(g + c);
+    u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = __uint_as_float(v[i] << 16) * inv * __uint_as_float(gv[i] << 16);
-      float b = __uint_as_float(v[i] & 0xffff0000u) * inv * __uint_as_float(gv[i] & 0xffff0000u);
-      o[i] = pack2(a, b);
+    for (int e = 0; e < 4; ++e) {
+      const float a = __uint_as_float(v[i][e] << 16) * inv * __uint_as_float(gv[e] << 16);
+      const float b = __uint_as_float(v[i][e] & 0xffff0000u) * inv * __uint_as_float(gv[e] & 0xffff0000u);
+      o[e] = pack2(a, b);
     }
     *reinterpret_cast<u32x4*>(yr + c) = o;
   }
 }
 
+template <int CH>
+__global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
+    int rows_padded, int hidden, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kNormRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= rows_padded) return;
+  bf16* yr = y + (size_t)r * hidden;
+  if (r >= rows) {  // padding row: zero dummy token
+    for (int c = lane * 8; c < hidden; c += 64 * 8) *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
+    return;
+  }
+  rmsnorm_row<CH>(x + (size_t)r * hidden, g, yr, hidden, eps, lane);
+}
+
+template <int CH>
+static void launch_norm(const bf16* x, const bf16* g, bf16* y, int rows, int rows_padded,
+                        int hidden, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel<CH>,
+                     dim3((rows_padded + kNormRowsPerBlock - 1) / kNormRowsPerBlock),
+                     dim3(64 * kNormRowsPerBlock), 0, s, x, g, y, rows, rows_padded, hidden, eps);
+}
+
 hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* y, int rows, int rows_padded,
                           int hidden, float eps, hipStream_t s) {
   if (rows_padded == 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows_padded), dim3(kNormThreads), 0, s, x, g, y, rows,
-                     hidden, eps);
+  const int ch = (hidden + 511) / 512;  // 16-byte chunks per lane
+  if (ch <= 1) launch_norm<1>(x, g, y, rows, rows_padded, hidden, eps, s);
+  else if (ch <= 2) launch_norm<2>(x, g, y, rows, rows_padded, hidden, eps, s);
+  else if (ch <= 4) launch_norm<4>(x, g, y, rows, rows_padded, hidden, eps, s);
+  else if (ch <= 8) launch_norm<8>(x, g, y, rows, rows_padded, hidden, eps, s);
+  else if (ch <= 16) launch_norm<16>(x, g, y, rows, rows_padded, hidden, eps, s);
+  else if (ch <= kNormMaxChunks) launch_norm<kNormMaxChunks>(x, g, y, rows, rows_padded, hidden, eps, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------- RoPE + append
-// One block per row.  Pair i (< d/2) of a head rotates (u_i, u_{i+d/2}) by
-// pos * theta^(-2i/d); the angle and its sine/cosine are taken in fp64 so
-// long positions lose no precision.  Rotated q and k go back into qkv; K and
-// V go to the row's slot (V dimension-major inside the page).
+// One workgroup per row.  Pair i turns by pos * theta^(-2i/d): the row's d/2
+// angles are formed and reduced modulo 2*pi in fp64 (positions up to millions
+// keep full precision), their cos/sin taken once in fp32 and shared by every
+// head through LDS.  A thread then takes 8 consecutive pairs of one head:
+// 16-byte loads of u[i .. i+8) and u[i+d/2 .. i+d/2+8).
+// Rotated q and k go back into qkv; K and V go to the row's KV slot (V
+// dimension-major inside the page).
 __global__ __launch_bounds__(256) void rope_kv_append_kernel(
     bf16* __restrict__ qkv, const int32_t* __restrict__ pos_in, const int32_t* __restrict__ slot_in,
-    int nq, int nkv, int d, float theta, KvDev kv) {
+    ChunkList chunks, DecDev dec, int nq, int nkv, int d, float theta, KvDev kv) {
   const int r = blockIdx.x;
   const int half = d >> 1;
+  const int groups = half / 8;  // 8-pair groups per head
   const int ld = (nq + 2 * nkv) * d;
   bf16* row = qkv + (size_t)r * ld;
-  const int pos = pos_in[r];
-  const int slot = slot_in[r];
+  int pos, slot;
+  if (pos_in) {
+    pos = pos_in[r];
+    slot = slot_in[r];
+  } else {
+    row_pos_slot(chunks, dec, kv.page_size, kv.num_pages, r, &pos, &slot);
+  }
   const int page = slot >= 0 ? slot / kv.page_size : -1;
   const int off = slot >= 0 ? slot % kv.page_size : 0;
-  const double ln_theta = log((double)theta);
-  // rotations of the nq q heads and the nkv k heads
-  for (int p = threadIdx.x; p < (nq + nkv) * half; p += blockDim.x) {
-    const int h = p / half, i = p % half;
-    const double ang = (double)pos * exp(-2.0 * (double)i / (double)d * ln_theta);
-    double sd, cd;
-    sincos(ang, &sd, &cd);
-    const float c = (float)cd, s = (float)sd;
+  __shared__ float cs_tab[64], sn_tab[64];  // d/2 <= 64
+  if (threadIdx.x < half) {
+    const double two_pi = 6.283185307179586476925;
+    const double inv_freq = exp2(-2.0 * (double)threadIdx.x / (double)d * log2((double)theta));
+    double ang = (double)pos * inv_freq;
+    ang -= two_pi * floor(ang / two_pi);
+    sincosf((float)ang, &sn_tab[threadIdx.x], &cs_tab[threadIdx.x]);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < (nq + nkv) * groups; t += blockDim.x) {
+    const int h = t / groups, i0 = (t % groups) * 8;
     bf16* u = row + h * d;
-    const float a = bf2f(u[i]), b = bf2f(u[i + half]);
-    const bf16 ra = f2bf(a * c - b * s), rb = f2bf(a * s + b * c);
-    u[i] = ra;
-    u[i + half] = rb;
+    const u32x4 av = ld16(u + i0), bv = ld16(u + i0 + half);
+    float a[8], b[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[2 * e] = __uint_as_float(av[e] << 16);
+      a[2 * e + 1] = __uint_as_float(av[e] & 0xffff0000u);
+      b[2 * e] = __uint_as_float(bv[e] << 16);
+      b[2 * e + 1] = __uint_as_float(bv[e] & 0xffff0000u);
+    }
+    float ra[8], rb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float cs = cs_tab[i0 + e], sn = sn_tab[i0 + e];
+      ra[e] = a[e] * cs - b[e] * sn;
+      rb[e] = a[e] * sn + b[e] * cs;
+    }
+    u32x4 oa, ob;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      oa[e] = pack2(ra[2 * e], ra[2 * e + 1]);
+      ob[e] = pack2(rb[2 * e], rb[2 * e + 1]);
+    }
+    *reinterpret_cast<u32x4*>(u + i0) = oa;
+    *reinterpret_cast<u32x4*>(u + i0 + half) = ob;
     if (h >= nq && page >= 0) {
       bf16* kp = kv.k_page(page, h - nq) + (size_t)off * d;
-      kp[i] = ra;
-      kp[i + half] = rb;
+      *reinterpret_cast<u32x4*>(kp + i0) = oa;
+      *reinterpret_cast<u32x4*>(kp + i0 + half) = ob;
     }
   }
   if (page >= 0) {
@@ -140,8 +207,21 @@ hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* s
                                  int nq, int nkv, int d, float theta, const KvDev& kv,
                                  hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_kv_append_kernel, dim3(rows), dim3(256), 0, s, qkv, pos, slot, nq, nkv,
-                     d, theta, kv);
+  ChunkList none_c;
+  memset(&none_c, 0, sizeof(none_c));
+  DecDev none_d{};
+  hipLaunchKernelGGL(rope_kv_append_kernel, dim3(rows), dim3(256), 0, s, qkv, pos, slot, none_c,
+                     none_d, nq, nkv, d, theta, kv);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv_append_meta(bf16* qkv, const ChunkList& chunks, const DecDev& dec,
+                                      int nq, int nkv, int d, float theta, const KvDev& kv,
+                                      hipStream_t s) {
+  const int rows = chunks.n_rows + dec.n;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_kv_append_kernel, dim3(rows), dim3(256), 0, s, qkv, nullptr, nullptr,
+                     chunks, dec, nq, nkv, d, theta, kv);
   return hipGetLastError();
 }
 

@@ -71,7 +71,9 @@ class Stage:
 def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ffn: int,
                  chunk_lens: Sequence[int], chunk_starts: Sequence[int],
                  ctx_lens: Sequence[int], pad: int = 16) -> List[Stage]:
-    """Algorithmic flops and bytes of every kernel of one layer call."""
+    """Algorithmic flops and bytes of every step of one layer call, named and
+    grouped as the library runs them (prefill and decode attention share one
+    launch; the O projection and the second RMSNorm share one step)."""
     H, nq, nkv, d, F = hidden, n_q_heads, n_kv_heads, head_dim, ffn
     Lp = int(sum(chunk_lens))
     Bd = len(ctx_lens)
@@ -89,11 +91,14 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     for L, P0 in zip(chunk_lens, chunk_starts):
         pf_flops += 4.0 * d * nq * (L * P0 + L * (L + 1) / 2)
         pf_bytes += (P0 + L) * kvB + 2 * L * nq * d * 2
-    st.append(Stage("prefill_attn", pf_flops, pf_bytes))
     keys = sum(int(c) + 1 for c in ctx_lens)
-    st.append(Stage("decode_attn", 4.0 * d * nq * keys, keys * kvB + 2 * Bd * nq * d * 2))
-    st.append(Stage("gemm_o", 2 * Mp * nq * d * H, nq * d * H * 2 + M * nq * d * 2 + 2 * M * H * 2))
-    st.append(Stage("rmsnorm2", 3 * M * H, 2 * M * H * 2 + H * 2))
+    dc_flops = 4.0 * d * nq * keys
+    dc_bytes = keys * kvB + 2 * Bd * nq * d * 2
+    # prefill and decode rows run in one launch and overlap: priced together
+    st.append(Stage("attention", pf_flops + dc_flops, pf_bytes + dc_bytes))
+    # O projection + residual, then RMSNorm of h: attn in, x in, h out, xn2 out
+    st.append(Stage("gemm_o_rmsnorm2", 2 * Mp * nq * d * H + 3 * M * H,
+                    nq * d * H * 2 + M * nq * d * 2 + 3 * M * H * 2 + H * 2))
     st.append(Stage("gemm_gate_up", 2 * Mp * H * 2 * F, 2 * F * H * 2 + M * H * 2 + M * F * 2))
     st.append(Stage("gemm_down", 2 * Mp * F * H, F * H * 2 + M * F * 2 + 2 * M * H * 2))
     for s in st:

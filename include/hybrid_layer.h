@@ -139,15 +139,27 @@ int hl_workspace_bytes(const hl_config* cfg, int32_t max_rows, int32_t max_decod
  *       dec->max_ctx, pad), 256-byte aligned;
  *   pad row padding: the GEMMs run on Mp = ceil(M/pad)*pad rows, the pad rows
  *       being zero dummy tokens that write no KV and reach no output.
- * Steps, all on `stream`: positions and KV slots; RMSNorm; fused QKV GEMM;
- * RoPE on q and k + append of K/V into the pages; chunk-prefill attention
- * (causal within the chunk, paged KV of earlier chunks); paged split-K
- * decode attention; O GEMM + residual; RMSNorm; gate/up GEMM + SwiGLU; down
- * GEMM + residual.  Writes exactly M KV slots. */
+ * Steps, all on `stream`: RMSNorm; fused QKV GEMM; each row's position and
+ * KV slot, RoPE on q and k and append of K/V into the pages; attention -- the
+ * chunk-prefill rows (causal within the chunk, paged KV of earlier chunks)
+ * and the paged split-K decode rows in one launch; O GEMM + residual and
+ * RMSNorm; gate/up GEMM + SwiGLU; down GEMM + residual.  Writes exactly M KV
+ * slots. */
 int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
                      const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
                      const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
                      const hl_taps* taps, hipStream_t stream);
+
+/* The same forward, recording stage_events[i] (caller-created HIP events,
+ * HL_N_STAGES + 1 of them) on `stream` before step i and stage_events
+ * [HL_N_STAGES] after the last, so that the caller can time every step of the
+ * real sequence.  hl_stage_name(i) names step i. */
+#define HL_N_STAGES 7
+int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                           const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                           const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
+                           const hl_taps* taps, hipEvent_t* stage_events, hipStream_t stream);
+const char* hl_stage_name(int stage);
 
 /* Row positions and KV slots of a hybrid batch (PagedAttention addressing:
  * slot = block_table[pos / page_size] * page_size + pos % page_size).

@@ -238,3 +238,50 @@ def test_validate_metadata():
     bad[1, 0] = int(hb.chunks[0].block_table[0])
     dec = B.hl_decodes(db.dec.n, db.dec.ctx_lens, bad.data_ptr(), db.dec.max_blocks, db.dec.max_ctx)
     assert B.hl_validate_metadata(db.cfg, db.chunks, dec, hb.num_pages) == -6
+
+
+def test_timed_forward_matches_plain_forward():
+    """The stage-event variant runs the same kernels: identical output and KV."""
+    import torch
+    hb = mistral_batch(seed=3, prior_kv="random")
+    db = B.DeviceBatch(hb)
+    db.forward()
+    torch.cuda.synchronize()
+    out_plain = db.out.clone()
+    kv_plain = db.kv_t.clone()
+    db.kv_t.copy_(B.bits_to_device(B.kv_to_library_layout(hb.kv_pages)))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(B.N_STAGES + 1)]
+    for e in evs:
+        e.record()
+    B.hl_layer_forward_timed(db.cfg, db.weights, db.x, db.chunks, db.dec, db.kv, db.out, db.ws,
+                             db.ws_bytes, db.pad, evs)
+    torch.cuda.synchronize()
+    assert torch.equal(db.out.view(torch.int16), out_plain.view(torch.int16))
+    assert torch.equal(db.kv_t.view(torch.int16), kv_plain.view(torch.int16))
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(B.N_STAGES)]
+    assert all(t >= 0 for t in times)
+    assert B.stage_names()[-1] == "gemm_down"
+
+
+def test_prefill_attention_without_split_long_prefix():
+    """Standalone prefill attention with no workspace (no key split): one
+    wave walks > 1024 keys, refilling its block-table window."""
+    import torch
+    hb = make_hybrid_batch(TINY, chunk_lens=[32], chunk_starts=[2500], n_decodes=0, seed=28,
+                           random_gains=True)
+    db, gpu = run_gpu(hb)
+    ref = run_oracle(hb)
+    attn = torch.zeros((db.Mp, TINY.n_q_heads * TINY.head_dim), dtype=torch.bfloat16,
+                       device="cuda")
+    B.hl_prefill_attention(db.cfg, db.tap_t["qkv"], db.chunks, db.kv, attn)
+    torch.cuda.synchronize()
+    assert_close("attn (unsplit)", tap_f64(attn, db.M), ref.taps["attn"])
+    assert_close("attn (layer)", gpu["attn"], ref.taps["attn"])
+
+
+def test_layer_llama70_full_size():
+    _flush("llama2-70b-shaped: Lp=512 after 3584 cached + 64 decodes ctx U[512,4096]")
+    from chunked_prefill_hybrid_rmsnorm_amd.inputs import llama70_batch
+    hb = llama70_batch(seed=0, random_gains=True)
+    _, gpu = run_gpu(hb)
+    check_layer(hb, gpu, run_oracle(hb))
