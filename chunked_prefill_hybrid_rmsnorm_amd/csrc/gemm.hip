@@ -121,8 +121,8 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_norm(
 // Row tile: 288 rows (one tile spans a whole hybrid batch of up to 288 rows,
 // so every weight tile is streamed from HBM once) or 128 rows for small
 // batches; 128 weight rows per tile.  K is split so that about one
-// workgroup per CU is resident (measured best on MI355X: 4 waves, 1 per SIMD,
-// with the copy pipeline hiding HBM latency), keeping >= 8 k-steps per split.
+// workgroup per CU is resident (measured best on MI355X: 8 waves of 144x32,
+// two per SIMD, behind a 3-stage copy ring), keeping >= 8 k-steps per split.
 struct Choice {
   int big;     // 1: 288-row tile, 0: 128-row tile
   int splits;  // K splits (1 = none)
@@ -150,7 +150,7 @@ template <int EPI>
 static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2,
                              bf16* c, const bf16* r, float* part, int m, int mp, int n, int k,
                              hipStream_t s) {
-  if (ch.big) return run_gemm_dma<288, 128, 2, 2, EPI, 3>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  if (ch.big) return run_gemm_dma<288, 128, 2, 4, EPI, 3>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
   return run_gemm_dma<128, 128, 2, 2, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
 }
 

@@ -10,11 +10,12 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 
 // Global -> LDS copies (global_load_lds_dwordx4, no
 // register staging) into a ring of STAGES buffers, so STAGES-1 k-steps of
-// loads are in flight while one is multiplied.  BK = 64: one tile row is 128 B
-// = 8 chunks of 16 B; chunk c of row r sits in slot c ^ (r % 8), which keeps
-// the 16-row fragment reads free of bank conflicts.  One copy instruction
-// fills 1 KB = 8 rows; wave w issues blocks w, w + NW, ...  Rows past the end
-// of A or W are clamped to the last valid row: their products only reach
+// loads are in flight while one is multiplied.  A stage holds BK (64 or 32)
+// values of K per row, i.e. 8 or 4 chunks of 16 B; one copy instruction fills
+// 1 KB = 8 or 16 rows.  Chunk c of row r sits in slot c ^ (r % 8) (BK 64) or
+// c ^ ((r / 4) % 4) (BK 32), which keeps the 16-row fragment reads free of
+// bank conflicts.  Wave w issues blocks w, w + NW, ...  Rows past the end of
+// A or W are clamped to the last valid row: their products only reach
 // outputs that are never stored.
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
@@ -28,23 +29,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES>
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return BK == 64 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 2) & 3));
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W2,
     bf16* __restrict__ C, const bf16* __restrict__ R, float* __restrict__ part, int M, int Mp,
     int N, int K, int n_mtiles, int n_ntiles, int splits) {
-  constexpr int BK = 64;
-  constexpr int NW = WM * WN;
+  static_assert(BK == 64 || BK == 32, "stage depth");
+  constexpr int ROWB = BK * 2;            // bytes of one tile row in a stage
+  constexpr int BLK_ROWS = 1024 / ROWB;   // rows per 1 KB copy block
+  constexpr int NCH = BK / 8;             // 16-byte chunks per row
+  constexpr int NW = WM * WN;  // waves in the workgroup
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  constexpr int A_BLK = BM / 8, W_BLK = BN / 8;  // 1 KB blocks per stage
+  constexpr int A_BLK = BM / BLK_ROWS, W_BLK = BN / BLK_ROWS;  // 1 KB blocks per stage
   constexpr int NBLK = A_BLK + W_BLK;
-  constexpr int PER_WAVE = NBLK / NW;             // copy instructions per wave per stage
+  // copy instructions per wave per stage: the first NBLK % NW waves take one more
+  constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
+  constexpr int PER_WAVE_LO = NBLK / NW;
   constexpr int STAGE_BYTES = NBLK * 1024;
-  static_assert(BM % 8 == 0 && BN % 8 == 0 && NBLK % NW == 0, "blocks must split evenly over waves");
+  static_assert(BM % BLK_ROWS == 0 && BN % BLK_ROWS == 0, "tiles are whole copy blocks");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole MFMA blocks");
-  static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && (BN / 2) % 8 == 0), "swiglu pairing");
+  static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && (BN / 2) % BLK_ROWS == 0), "swiglu pairing");
   static_assert(STAGES >= 3, "need at least three stages");
   static_assert(PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
 
@@ -76,9 +87,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
   const bf16* src[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int blk = wave + i * NW;
-    const int row = blk * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ (row & 7);
+    const int blk = min(wave + i * NW, NBLK - 1);
+    const int row = blk * BLK_ROWS + lane / NCH;
+    const int chunk = swz<BK>(row, lane % NCH);
     const bf16* p;
     if (blk < A_BLK) {
       const int m = min(m0 + row, Mp - 1);
@@ -102,8 +113,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     const int kt = kt0 + min(step, max(nk - 1, 0));
     char* st = smem + (step % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) lds_dma16(src[i] + kt * BK, st + (wave + i * NW) * 1024);
+    for (int i = 0; i < PER_WAVE; ++i)
+      if (wave + i * NW < NBLK) lds_dma16(src[i] + kt * BK, st + (wave + i * NW) * 1024);
   };
+  const bool more = (NBLK % NW) != 0 && wave < NBLK % NW;  // this wave copies PER_WAVE blocks
 
   f32x4 acc[FN][FM];
 #pragma unroll
@@ -116,7 +129,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int row = wm * WTM + fm * 16 + l16;
-    a_off[fm] = row * 128;
+    a_off[fm] = row * ROWB;
   }
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -128,25 +141,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
       row = wn * WTN + fn * 16;
     }
     row += l16;
-    w_off[fn] = (BM + row) * 128;
+    w_off[fn] = (BM + row) * ROWB;
   }
-  const int sw = l16 & 7;  // rows of a fragment are consecutive: row % 8 == l16 % 8 (+ const)
+  // fragment rows start at multiples of 16, so the swizzle depends on l16 only
 
   if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(s);
     for (int it = 0; it < nk; ++it) {
-      wait_vmcnt<PER_WAVE * (STAGES - 2)>();
+      if (PER_WAVE == PER_WAVE_LO || more)
+        wait_vmcnt<PER_WAVE * (STAGES - 2)>();
+      else
+        wait_vmcnt<PER_WAVE_LO * (STAGES - 2)>();
       asm volatile("" ::: "memory");  // keep LDS reads and copies on their side of the barrier
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       issue(it + STAGES - 1);
       const char* st = smem + (it % STAGES) * STAGE_BYTES;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < BK / 32; ++ks) {
         bf16x8 af[FN], bfr[FM];
-        const int c = ks * 4 + q;
-        const int so = ((c ^ sw) << 4);
+        const int so = swz<BK>(l16, ks * 4 + q) << 4;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) af[fn] = as_bf16x8(ld16(st + w_off[fn] + so));
 #pragma unroll
@@ -159,7 +174,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     }
   }
   wait_vmcnt<0>();  // drain the clamped tail copies before the workgroup ends
-
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int m = m0 + wm * WTM + fm * 16 + l16;
@@ -209,15 +223,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES>
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64>
 hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, const bf16* r,
                         float* part, int m, int mp, int n, int k, int splits, hipStream_t s) {
   constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  constexpr size_t lds = (size_t)STAGES * (BM + BN) * 128;
+  constexpr size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int mt = (mp + BM - 1) / BM, nt = (n + OUT_N - 1) / OUT_N;
   if (EPI == EPI_SWIGLU) splits = 1;
-  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES>;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK>;
   // raise the dynamic LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
