@@ -12,8 +12,10 @@ the KV pool are rotated so that the 256 MB MALL cannot hold one call's
 working set for the next.
 
 Printed: one JSON line with tokens/s per layer (real rows / time), the
-dominant kernel's roofline figures, per-kernel times against the roofline
-model T = max(T_math, T_mem), and the CPU oracle's rate on the host.
+dominant kernel's roofline figures, the time of every kernel slot of the
+layer against the roofline model T = max(T_math, T_mem), and the CPU
+oracle's rate on the host.  Kernel times come from HIP events that the
+library records between its kernels on the stream it launches on.
 """
 from __future__ import annotations
 
@@ -44,6 +46,8 @@ def parse():
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-runs", type=int, default=2)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run one 256 MiB device-to-device copy first (PMC byte-counter scale)")
     return p.parse_args()
 
 
@@ -72,6 +76,9 @@ def time_loop(fn, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def cpu_baseline(hb, runs):
@@ -106,6 +113,7 @@ def main():
         sys.exit(2)
     import torch
     from chunked_prefill_hybrid_rmsnorm_amd import binding as B
+    from chunked_prefill_hybrid_rmsnorm_amd import profiling as P
     from chunked_prefill_hybrid_rmsnorm_amd import roofline as RL
     if not torch.cuda.is_available():
         log("bench.py needs a GPU")
@@ -113,6 +121,13 @@ def main():
     B.load()
     torch.cuda.set_device(0)
 
+    if a.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"generating {a.workload} inputs ...")
     hb, desc = make_batch(a.workload)
     db = B.DeviceBatch(hb, pad=a.pad)
@@ -170,16 +185,18 @@ def main():
     for k, name in enumerate(names):
         t = sum(ev[k].elapsed_time(ev[k + 1]) for ev in ev_sets) / a.steps * 1e-3
         st = stages[name]
+        work = st.flops > 0 or st.bytes > 0
         table[name] = {
             "us": round(t * 1e6, 2),
-            "bound": st.bound,
+            "bound": st.bound if work else "none (launch-shape overhead)",
             "t_roof_us": round(st.t_roof() * 1e6, 2),
-            "roof_frac": round(st.t_roof() / t, 4) if t > 0 else None,
-            "GB/s": round(st.bytes / t / 1e9, 1) if t > 0 else None,
-            "TFLOP/s": round(st.flops / t / 1e12, 2) if t > 0 else None,
+            "roof_frac": round(st.t_roof() / t, 4) if t > 0 and work else None,
+            "GB/s": round(st.bytes / t / 1e9, 1) if t > 0 and work else None,
+            "TFLOP/s": round(st.flops / t / 1e12, 2) if t > 0 and work else None,
         }
-        log(f"  {name:16s} {t * 1e6:8.1f} us  roof {st.t_roof() * 1e6:7.1f} us  "
-            f"({st.bound}, frac {table[name]['roof_frac']})")
+        log(f"  {name:24s} {t * 1e6:8.1f} us  roof {st.t_roof() * 1e6:7.1f} us  "
+            f"({table[name]['bound']}, frac {table[name]['roof_frac']})")
+    # dominant kernel: the slot with the longest average duration
     dom = max(table, key=lambda k: table[k]["us"])
     st = stages[dom]
     t_dom = table[dom]["us"] * 1e-6
@@ -190,9 +207,12 @@ def main():
         roof = {"bound": "mfma", "achieved": round(st.flops / t_dom / 1e12, 2),
                 "peak": RL.PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = P.stored_traffic(TRAFFIC_FILE, dom)
     roof["kernel"] = dom
+    roof["kernel_us"] = table[dom]["us"]
     roof["algorithmic_per_launch"] = st.bytes if st.bound == "hbm" else st.flops
+    roof["algorithmic_bytes"] = st.bytes
+    roof["algorithmic_flops"] = st.flops
     t_roof = RL.layer_roofline_time(list(stages.values()))
 
     result = {

@@ -130,8 +130,9 @@ int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t m
 }
 
 static const char* const kStageNames[HL_N_STAGES] = {
-    "rmsnorm1", "gemm_qkv", "rope_kv_append", "attention", "gemm_o_rmsnorm2", "gemm_gate_up",
-    "gemm_down"};
+    "rmsnorm1",       "gemm_qkv",  "gemm_qkv_reduce",    "rope_kv_append",
+    "attention",      "attention_merge", "gemm_o",      "gemm_o_reduce_rmsnorm2",
+    "gemm_gate_up",   "gemm_down", "gemm_down_reduce"};
 
 const char* hl_stage_name(int stage) {
   return (stage >= 0 && stage < HL_N_STAGES) ? kStageNames[stage] : "";
@@ -189,41 +190,47 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
     ++stage;
     return true;
   };
+  // event between the two kernels of a two-kernel step (its slot boundary)
+  auto mid = [&]() -> hipEvent_t {
+    hipEvent_t m = ev ? ev[stage] : nullptr;
+    ++stage;
+    return m;
+  };
 #define HL_MARK() \
   do {            \
     if (!mark()) return HL_ERR_HIP; \
   } while (0)
   HL_MARK();
-  // a1: RMSNorm (pad rows -> 0)
+  // RMSNorm of the input rows (pad rows -> 0)
   HL_TRY(launch_rmsnorm(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
                         cfg->rms_eps, stream));
   HL_MARK();
-  // a2: fused QKV projection on the stacked rows
+  // fused QKV projection on the stacked rows, then the split-K reduce
   void* gws = base + L.gemm;
   HL_TRY(launch_gemm(EPI_STORE, xn1, reinterpret_cast<const bf16*>(w->w_qkv), nullptr, qkv,
-                     nullptr, gws, M, Mp, nqkv, H, stream));
+                     nullptr, gws, M, Mp, nqkv, H, stream, mid()));
   HL_MARK();
-  // a0 + a3: each row's position and KV slot, RoPE on q and k, append K and V
+  // each row's position and KV slot, RoPE on q and k, append K and V
   HL_TRY(launch_rope_kv_append_meta(qkv, cl, dd, nq, nkv, d, cfg->rope_theta, kvd, stream));
   HL_MARK();
-  // a4 + a5: chunk-prefill attention (rows [0, Lp)) and paged decode attention
+  // chunk-prefill attention (rows [0, Lp)) and paged decode attention
   // (rows [Lp, M)) in one launch
   HL_TRY(launch_attention(qkv, nq, nkv, d, cl, dd, cl.n_rows, kvd, attn, base + L.pre,
-                          base + L.dec, stream));
+                          base + L.dec, stream, mid()));
   HL_MARK();
-  // a6 + a7: O projection + residual, then RMSNorm (fused into the split-K reduce)
+  // O projection + residual, then RMSNorm (fused into the split-K reduce)
   HL_TRY(launch_gemm_residual_norm(attn, reinterpret_cast<const bf16*>(w->w_o), h, xin,
                                    reinterpret_cast<const bf16*>(w->g_ffn), xn2, cfg->rms_eps, gws,
-                                   M, Mp, H, nq * d, stream));
+                                   M, Mp, H, nq * d, stream, mid()));
   HL_MARK();
-  // a8: gate/up projection + SwiGLU
+  // gate/up projection + SwiGLU
   HL_TRY(launch_gemm(EPI_SWIGLU, xn2, reinterpret_cast<const bf16*>(w->w_gate),
                      reinterpret_cast<const bf16*>(w->w_up), act, nullptr, nullptr, M, Mp, F, H,
                      stream));
   HL_MARK();
-  // a9: down projection + residual
+  // down projection + residual
   HL_TRY(launch_gemm(EPI_RESIDUAL, act, reinterpret_cast<const bf16*>(w->w_down), nullptr,
-                     reinterpret_cast<bf16*>(out), h, gws, M, Mp, H, F, stream));
+                     reinterpret_cast<bf16*>(out), h, gws, M, Mp, H, F, stream, mid()));
   HL_MARK();
 #undef HL_MARK
 #undef HL_TRY

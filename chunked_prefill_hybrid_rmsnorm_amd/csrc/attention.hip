@@ -259,7 +259,7 @@ size_t decode_workspace_bytes(int n_decodes, int nq, int d, int max_ctx) {
 
 hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const ChunkList& chunks,
                             const DecDev& dec, int dec_row0, const KvDev& kv, bf16* attn,
-                            void* pf_ws, void* dc_ws, hipStream_t s) {
+                            void* pf_ws, void* dc_ws, hipStream_t s, hipEvent_t mid) {
   AttnArgs A;
   memset(&A, 0, sizeof(A));
   A.qkv = qkv;
@@ -295,16 +295,21 @@ hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const Chunk
     A.dc_ml = A.dc_o + (size_t)dec.n * nq * A.dc_parts * d;
   }
   const int wgs = A.pf_wgs + A.dc_wgs;
-  if (wgs == 0) return hipSuccess;
+  if (wgs == 0) return mid ? hipEventRecord(mid, s) : hipSuccess;
   const int merge_rows = chunks.n_rows + dec.n;
   const bool merge = A.pf_ns > 1 || A.dc_parts > 1;
-  if (d == 128) {
+  if (d == 128)
     hipLaunchKernelGGL(attention_kernel<128>, dim3(wgs), dim3(64 * kAttnWaves), 0, s, A);
-    if (merge) hipLaunchKernelGGL(attention_merge_kernel<128>, dim3(nq, merge_rows), dim3(64), 0, s, A);
-  } else {
+  else
     hipLaunchKernelGGL(attention_kernel<64>, dim3(wgs), dim3(64 * kAttnWaves), 0, s, A);
-    if (merge) hipLaunchKernelGGL(attention_merge_kernel<64>, dim3(nq, merge_rows), dim3(64), 0, s, A);
-  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
+  if (!merge) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL(attention_merge_kernel<128>, dim3(nq, merge_rows), dim3(64), 0, s, A);
+  else
+    hipLaunchKernelGGL(attention_merge_kernel<64>, dim3(nq, merge_rows), dim3(64), 0, s, A);
   return hipGetLastError();
 }
 

@@ -156,7 +156,7 @@ static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, con
 
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
                        const bf16* residual, void* ws, int m, int m_padded, int n, int k,
-                       hipStream_t s) {
+                       hipStream_t s, hipEvent_t mid) {
   if (m_padded == 0 || n == 0) return hipSuccess;
   Choice ch = choose(epi, m_padded, n, k);
   if (ch.splits > 1 && ws == nullptr) ch.splits = 1;
@@ -173,7 +173,9 @@ hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf1
       e = run_choice<EPI_SWIGLU>(ch, a, w, w2, c, nullptr, part, m, m_padded, n, k, s);
       break;
   }
-  if (e != hipSuccess || ch.splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
+  if (ch.splits == 1) return hipSuccess;
   const int mlim = epi == EPI_RESIDUAL ? m : m_padded;
   const int threads = mlim * (n / 4);
   if (threads == 0) return hipSuccess;
@@ -195,18 +197,20 @@ static void launch_rn(const float* part, int splits, bf16* h, const bf16* r, con
 
 hipError_t launch_gemm_residual_norm(const bf16* a, const bf16* w, bf16* h, const bf16* residual,
                                      const bf16* g, bf16* y, float eps, void* ws, int m,
-                                     int m_padded, int n, int k, hipStream_t s) {
+                                     int m_padded, int n, int k, hipStream_t s, hipEvent_t mid) {
   if (m_padded == 0 || n == 0) return hipSuccess;
   Choice ch = choose(EPI_RESIDUAL, m_padded, n, k);
   const int nch = (n + 2047) / 2048;  // 8-column chunks per thread
   if (ch.splits == 1 || ws == nullptr || nch > 8) {
-    hipError_t e = launch_gemm(EPI_RESIDUAL, a, w, nullptr, h, residual, ws, m, m_padded, n, k, s);
+    hipError_t e = launch_gemm(EPI_RESIDUAL, a, w, nullptr, h, residual, ws, m, m_padded, n, k, s,
+                               mid);
     if (e != hipSuccess) return e;
     return launch_rmsnorm(h, g, y, m, m_padded, n, eps, s);
   }
   float* part = reinterpret_cast<float*>(ws);
   hipError_t e = run_choice<EPI_RESIDUAL>(ch, a, w, nullptr, h, residual, part, m, m_padded, n, k, s);
   if (e != hipSuccess) return e;
+  if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   if (nch <= 1) launch_rn<1>(part, ch.splits, h, residual, g, y, m, m_padded, n, eps, s);
   else if (nch <= 2) launch_rn<2>(part, ch.splits, h, residual, g, y, m, m_padded, n, eps, s);
   else if (nch <= 4) launch_rn<4>(part, ch.splits, h, residual, g, y, m, m_padded, n, eps, s);

@@ -22,16 +22,19 @@ hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* y, int rows, int r
 enum GemmEpilogue { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
 // c = a w^T (+ residual) / swiglu(a w_gate^T, a w_up^T).  ws holds split-K
 // partials (gemm_workspace_bytes); with ws == nullptr K is not split.
+// Launchers of two kernels record `mid` (when not null) on the stream between
+// the first and the second, also when the second is not needed.
 size_t gemm_workspace_bytes(GemmEpilogue epi, int m_padded, int n, int k);
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
                        const bf16* residual, void* ws, int m, int m_padded, int n, int k,
-                       hipStream_t s);
+                       hipStream_t s, hipEvent_t mid = nullptr);
 
 // h = a w^T + residual (rows < m) followed by y = RMSNorm(h; g, eps) (rows
 // < m_padded, pad rows zero); with split K the norm runs inside the reduce.
 hipError_t launch_gemm_residual_norm(const bf16* a, const bf16* w, bf16* h, const bf16* residual,
                                      const bf16* g, bf16* y, float eps, void* ws, int m,
-                                     int m_padded, int n, int k, hipStream_t s);
+                                     int m_padded, int n, int k, hipStream_t s,
+                                     hipEvent_t mid = nullptr);
 
 hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* slot, int rows,
                                  int nq, int nkv, int d, float theta, const KvDev& kv,
@@ -53,7 +56,7 @@ size_t decode_workspace_bytes(int n_decodes, int nq, int d, int max_ctx);
 // split); pf_ws / dc_ws as for the two launchers below.
 hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const ChunkList& chunks,
                             const DecDev& dec, int dec_row0, const KvDev& kv, bf16* attn,
-                            void* pf_ws, void* dc_ws, hipStream_t s);
+                            void* pf_ws, void* dc_ws, hipStream_t s, hipEvent_t mid = nullptr);
 hipError_t launch_decode_attention(const bf16* qkv, int row0, int nq, int nkv, int d,
                                    const DecDev& dec, const KvDev& kv, bf16* attn, void* ws,
                                    hipStream_t s);

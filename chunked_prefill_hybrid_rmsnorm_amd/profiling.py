@@ -1,0 +1,251 @@
+"""Turn rocprofv3 output for the layer into per-kernel-slot summaries.
+
+The library launches at most one kernel per slot (``hl_stage_name``), in a
+fixed order per layer call.  rocprofv3 names kernels, not slots, and one
+kernel template can fill two slots (the residual GEMM runs both the O and the
+down projection), so each dispatch is labelled from its name and the slot
+that came before it in the same call.
+
+Inputs are rocprofv3 CSV files:
+
+* ``--kernel-trace --stats`` -> ``*_kernel_trace.csv`` (durations), and
+* ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` -> ``*_counter_collection.csv``
+  (KiB per dispatch).  Both byte counters are scaled by what they read for a
+  plain device-to-device copy of 256 MiB that the profiled program runs first
+  (``bench.py --calibrate-copy``): the counters' units and coverage differ
+  from one chip to another, a copy of known size does not.
+
+Usage::
+
+    python -m chunked_prefill_hybrid_rmsnorm_amd.profiling \\
+        --trace kt_kernel_trace.csv --fetch f_counter_collection.csv \\
+        --write w_counter_collection.csv --workload "..." --command "..." \\
+        --md profiles/layer_kernels_mistral7b.md --traffic profiles/traffic.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+from typing import Dict, Iterable, List, Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+SLOTS = ("rmsnorm1", "gemm_qkv", "gemm_qkv_reduce", "rope_kv_append", "attention",
+         "attention_merge", "gemm_o", "gemm_o_reduce_rmsnorm2", "gemm_gate_up", "gemm_down",
+         "gemm_down_reduce")
+CALIBRATION_BYTES = 256 << 20
+
+
+def source_hash() -> str:
+    """Digest of every source the kernels and their launch shapes come from."""
+    h = hashlib.sha256()
+    files = []
+    for d in (os.path.join(PKG, "csrc"), os.path.join(ROOT, "include")):
+        files += [os.path.join(d, f) for f in sorted(os.listdir(d))
+                  if f.endswith((".hip", ".h"))]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _base_name(name: str) -> str:
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def _gemm_epilogue(name: str) -> Optional[int]:
+    m = re.search(r"gemm_dma_kernel<([^>]*)>", name)
+    if not m:
+        return None
+    return int(m.group(1).split(",")[4])
+
+
+class SlotLabeler:
+    """Labels the library's dispatches, one call after another."""
+
+    def __init__(self):
+        self.last = -1  # slot index of the previous dispatch of this call
+
+    def label(self, kernel_name: str) -> Optional[str]:
+        n = _base_name(kernel_name)
+        if not n.startswith("hl::"):
+            return None
+        idx = SLOTS.index
+        if "rmsnorm_kernel" in n:
+            # the second RMSNorm runs as a plain kernel when the O projection
+            # was not split
+            s = "gemm_o_reduce_rmsnorm2" if self.last == idx("gemm_o") else "rmsnorm1"
+        elif "gemm_splitk_reduce_norm" in n:
+            s = "gemm_o_reduce_rmsnorm2"
+        elif "gemm_splitk_reduce<0>" in n:
+            s = "gemm_qkv_reduce"
+        elif "gemm_splitk_reduce<1>" in n:
+            s = "gemm_down_reduce"
+        elif "rope_kv_append" in n:
+            s = "rope_kv_append"
+        elif "attention_merge" in n:
+            s = "attention_merge"
+        elif "attention_kernel" in n:
+            s = "attention"
+        elif "gemm_dma_kernel" in n:
+            epi = _gemm_epilogue(kernel_name)
+            if epi == 0:
+                s = "gemm_qkv"
+            elif epi == 2:
+                s = "gemm_gate_up"
+            else:
+                s = "gemm_down" if self.last >= idx("gemm_gate_up") else "gemm_o"
+        elif "slot_map" in n:
+            return None
+        else:
+            return None
+        self.last = idx(s)
+        return s
+
+
+def _rows(path: str) -> List[dict]:
+    with open(path, newline="") as f:
+        rows = list(csv.DictReader(f))
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else None
+    if key:
+        rows.sort(key=lambda r: int(r[key]))
+    return rows
+
+
+def kernel_durations(trace_csv: str) -> Dict[str, List[float]]:
+    """Per slot, the duration (ns) of every dispatch in a kernel trace."""
+    lab = SlotLabeler()
+    out: Dict[str, List[float]] = defaultdict(list)
+    for r in _rows(trace_csv):
+        s = lab.label(r["Kernel_Name"])
+        if s:
+            out[s].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    return out
+
+
+def counter_values(counter_csv: str, counter: str) -> Tuple[Dict[str, List[float]], float]:
+    """Per slot, the counter's value (KiB) of every dispatch, and the value of
+    the largest plain copy (the 256 MiB calibration copy)."""
+    lab = SlotLabeler()
+    out: Dict[str, List[float]] = defaultdict(list)
+    calib = 0.0
+    for r in _rows(counter_csv):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        if "copyBuffer" in r["Kernel_Name"]:
+            calib = max(calib, v)
+            continue
+        s = lab.label(r["Kernel_Name"])
+        if s:
+            out[s].append(v)
+    return out, calib
+
+
+def _mean(v: Iterable[float]) -> float:
+    v = list(v)
+    return sum(v) / len(v) if v else 0.0
+
+
+def summarize(trace_csv: Optional[str], fetch_csv: Optional[str], write_csv: Optional[str]):
+    res = {"slots": {}}
+    durs = kernel_durations(trace_csv) if trace_csv else {}
+    fetch, fcal = counter_values(fetch_csv, "FETCH_SIZE") if fetch_csv else ({}, 0.0)
+    write, wcal = counter_values(write_csv, "WRITE_SIZE") if write_csv else ({}, 0.0)
+    fscale = CALIBRATION_BYTES / (fcal * 1024) if fcal else None
+    wscale = CALIBRATION_BYTES / (wcal * 1024) if wcal else None
+    res["fetch_scale"] = fscale
+    res["write_scale"] = wscale
+    for s in SLOTS:
+        e = {}
+        if s in durs:
+            d = durs[s]
+            e.update(calls=len(d), avg_us=_mean(d) / 1e3, min_us=min(d) / 1e3, max_us=max(d) / 1e3)
+        if s in fetch and fscale:
+            e["fetch_bytes"] = _mean(fetch[s]) * 1024 * fscale
+        if s in write and wscale:
+            e["write_bytes"] = _mean(write[s]) * 1024 * wscale
+        if "fetch_bytes" in e and "write_bytes" in e:
+            e["traffic_bytes"] = e["fetch_bytes"] + e["write_bytes"]
+        if e:
+            res["slots"][s] = e
+    return res
+
+
+def write_markdown(path: str, res: dict, workload: str, commands: List[str]) -> None:
+    lines = [f"# Layer kernels, {workload}", "", "Commands (run from the repository root):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", f"Kernel sources digest: `{source_hash()}`", ""]
+    if res.get("fetch_scale"):
+        lines += [f"Byte-counter scale from the 256 MiB copy: FETCH_SIZE x{res['fetch_scale']:.4f}, "
+                  f"WRITE_SIZE x{res['write_scale']:.4f}", ""]
+    lines += ["| slot | calls | avg us | min us | max us | HBM read MB | HBM write MB |",
+              "|---|---:|---:|---:|---:|---:|---:|"]
+    tot = 0.0
+    for s in SLOTS:
+        e = res["slots"].get(s)
+        if not e:
+            continue
+        tot += e.get("avg_us", 0.0)
+        f = f"{e['fetch_bytes'] / 1e6:.1f}" if "fetch_bytes" in e else "-"
+        w = f"{e['write_bytes'] / 1e6:.1f}" if "write_bytes" in e else "-"
+        if "avg_us" in e:
+            lines.append(f"| {s} | {e['calls']} | {e['avg_us']:.2f} | {e['min_us']:.2f} | "
+                         f"{e['max_us']:.2f} | {f} | {w} |")
+        else:
+            lines.append(f"| {s} | - | - | - | - | {f} | {w} |")
+    lines += ["", f"Sum of slot averages: {tot:.1f} us per layer call.", ""]
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+
+
+def write_traffic(path: str, res: dict, workload: str) -> None:
+    kern = {s: {"traffic_bytes": round(e["traffic_bytes"]),
+                "fetch_bytes": round(e["fetch_bytes"]), "write_bytes": round(e["write_bytes"])}
+            for s, e in res["slots"].items() if "traffic_bytes" in e}
+    with open(path, "w") as fh:
+        json.dump({"source_sha": source_hash(), "workload": workload,
+                   "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"],
+                   "kernels": kern}, fh, indent=1)
+        fh.write("\n")
+
+
+def stored_traffic(path: str, slot: str) -> Optional[float]:
+    """HBM bytes per launch of `slot` from a committed measurement, or None
+    when there is none or any kernel source changed since it was taken."""
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_hash():
+        return None
+    e = t.get("kernels", {}).get(slot)
+    return e.get("traffic_bytes") if e else None
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--trace")
+    p.add_argument("--fetch")
+    p.add_argument("--write")
+    p.add_argument("--workload", required=True)
+    p.add_argument("--command", action="append", default=[])
+    p.add_argument("--md")
+    p.add_argument("--traffic")
+    a = p.parse_args()
+    res = summarize(a.trace, a.fetch, a.write)
+    if a.md:
+        write_markdown(a.md, res, a.workload, a.command)
+    if a.traffic:
+        write_traffic(a.traffic, res, a.workload)
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,7 @@ equation; the worked example of the SARATHI summary on gitcode.csdn.net,
 part 3, prices each batch the same way).  Kernels on one stream run back to
 back, so a layer's time at roofline is the sum over its kernels.
 
-Algorithmic work per kernel (real rows only unless stated):
+Algorithmic work per operation (real rows only unless stated):
 
 * GEMM ``[M,K] x [K,N]``: ``2*Mp*K*N`` flops (``Mp`` = rows after padding,
   what the hardware computes) and ``K*N*2 + M*K*2 + M*N*2`` bytes (weights
@@ -71,9 +71,15 @@ class Stage:
 def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ffn: int,
                  chunk_lens: Sequence[int], chunk_starts: Sequence[int],
                  ctx_lens: Sequence[int], pad: int = 16) -> List[Stage]:
-    """Algorithmic flops and bytes of every step of one layer call, named and
-    grouped as the library runs them (prefill and decode attention share one
-    launch; the O projection and the second RMSNorm share one step)."""
+    """Algorithmic flops and bytes of every kernel slot of one layer call, in
+    the library's launch order and under its slot names.
+
+    Each byte and flop of the layer is given to exactly one kernel: a GEMM's
+    main kernel carries the whole projection (weights, activations in, result
+    out, residual in); a split-K reduce carries only what its fused epilogue
+    adds to the algorithm (the second RMSNorm's output and gain), so a plain
+    reduce and the attention key-split merge carry none -- their time is
+    overhead of the launch shape, not work of the layer."""
     H, nq, nkv, d, F = hidden, n_q_heads, n_kv_heads, head_dim, ffn
     Lp = int(sum(chunk_lens))
     Bd = len(ctx_lens)
@@ -84,6 +90,7 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     st: List[Stage] = []
     st.append(Stage("rmsnorm1", 3 * M * H, 2 * M * H * 2 + H * 2))
     st.append(Stage("gemm_qkv", 2 * Mp * H * nqkv, H * nqkv * 2 + M * H * 2 + M * nqkv * 2))
+    st.append(Stage("gemm_qkv_reduce", 0.0, 0.0))
     st.append(Stage("rope_kv_append", 6 * M * (nq + nkv) * d,
                     M * nqkv * 2 + M * (nq + nkv) * d * 2 + M * kvB))
     pf_flops = 0.0
@@ -96,13 +103,16 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     dc_bytes = keys * kvB + 2 * Bd * nq * d * 2
     # prefill and decode rows run in one launch and overlap: priced together
     st.append(Stage("attention", pf_flops + dc_flops, pf_bytes + dc_bytes))
-    # O projection + residual, then RMSNorm of h: attn in, x in, h out, xn2 out
-    st.append(Stage("gemm_o_rmsnorm2", 2 * Mp * nq * d * H + 3 * M * H,
-                    nq * d * H * 2 + M * nq * d * 2 + 3 * M * H * 2 + H * 2))
+    st.append(Stage("attention_merge", 0.0, 0.0))
+    # O projection + residual: weights, attn in, x in, h out
+    st.append(Stage("gemm_o", 2 * Mp * nq * d * H, nq * d * H * 2 + M * nq * d * 2 + 2 * M * H * 2))
+    # RMSNorm of h inside the reduce: xn2 out and the gain
+    st.append(Stage("gemm_o_reduce_rmsnorm2", 3 * M * H, M * H * 2 + H * 2))
     st.append(Stage("gemm_gate_up", 2 * Mp * H * 2 * F, 2 * F * H * 2 + M * H * 2 + M * F * 2))
     st.append(Stage("gemm_down", 2 * Mp * F * H, F * H * 2 + M * F * 2 + 2 * M * H * 2))
+    st.append(Stage("gemm_down_reduce", 0.0, 0.0))
     for s in st:
-        s.bound = "mfma" if s.t_math() >= s.t_mem() else "hbm"
+        s.bound = "mfma" if s.t_math() > s.t_mem() else "hbm"
     return st
 
 

@@ -151,10 +151,13 @@ int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x
                      const hl_taps* taps, hipStream_t stream);
 
 /* The same forward, recording stage_events[i] (caller-created HIP events,
- * HL_N_STAGES + 1 of them) on `stream` before step i and stage_events
- * [HL_N_STAGES] after the last, so that the caller can time every step of the
- * real sequence.  hl_stage_name(i) names step i. */
-#define HL_N_STAGES 7
+ * HL_N_STAGES + 1 of them) on `stream` before kernel slot i and stage_events
+ * [HL_N_STAGES] after the last, so that the caller can time every kernel of
+ * the real sequence.  A slot holds at most one kernel; a slot whose kernel is
+ * not needed for this batch (a split-K reduce or a key-split merge that the
+ * launch shape makes unnecessary) times as an empty interval.  hl_stage_name(i)
+ * names slot i. */
+#define HL_N_STAGES 11
 int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
                            const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
                            const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,

@@ -36,6 +36,16 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(B.EXPORTED)
 
 
+def test_stage_slots_match_header(lib):
+    """The binding's slot count is the header's, every slot has a distinct
+    name, and the slots out of range have none."""
+    n = int(re.search(r"#define\s+HL_N_STAGES\s+(\d+)", open(HEADER).read()).group(1))
+    assert n == B.N_STAGES
+    names = B.stage_names()
+    assert len(names) == n and len(set(names)) == n and all(names)
+    assert lib.hl_stage_name(n) == b"" and lib.hl_stage_name(-1) == b""
+
+
 def test_error_strings(lib):
     for code in range(0, -8, -1):
         assert B.error_string(code) not in ("", "unknown error")
@@ -121,3 +131,10 @@ def test_kv_layout_roundtrip():
     flat = lib_layout.reshape(3, -1)
     v_base = 2 * 16 * 64 + 1 * 64 * 16
     assert flat[1, v_base + 7 * 16 + 5] == kv[1, 1, 1, 5, 7]
+
+
+def test_cost_model_slots_are_library_slots(lib):
+    from chunked_prefill_hybrid_rmsnorm_amd import profiling
+    from chunked_prefill_hybrid_rmsnorm_amd import roofline as rl
+    s = rl.layer_stages(4096, 32, 8, 128, 14336, [256], [768], [1000] * 32)
+    assert [x.name for x in s] == B.stage_names() == list(profiling.SLOTS)

@@ -260,7 +260,11 @@ def test_timed_forward_matches_plain_forward():
     assert torch.equal(db.kv_t.view(torch.int16), kv_plain.view(torch.int16))
     times = [evs[i].elapsed_time(evs[i + 1]) for i in range(B.N_STAGES)]
     assert all(t >= 0 for t in times)
-    assert B.stage_names()[-1] == "gemm_down"
+    names = B.stage_names()
+    assert len(set(names)) == B.N_STAGES and names[-1] == "gemm_down_reduce"
+    # this batch splits K in the QKV, O and down projections and splits keys
+    # in attention: every slot holds a kernel
+    assert all(t > 0 for t in times)
 
 
 def test_prefill_attention_without_split_long_prefix():

@@ -1,0 +1,37 @@
+"""Labelling of profiled dispatches with the library's kernel slots (CPU)."""
+from chunked_prefill_hybrid_rmsnorm_amd.profiling import SLOTS, SlotLabeler
+
+GEMM = "void hl::gemm_dma_kernel<288, 128, 2, 4, {e}, 3, 64>(unsigned short const*, int)"
+SPLIT_CALL = [
+    "void hl::rmsnorm_kernel<8>(unsigned short const*)",
+    GEMM.format(e=0),
+    "void hl::gemm_splitk_reduce<0>(float const*, int)",
+    "hl::rope_kv_append_kernel(unsigned short*, int const*)",
+    "void hl::attention_kernel<128>(hl::AttnArgs)",
+    "void hl::attention_merge_kernel<128>(hl::AttnArgs)",
+    GEMM.format(e=1),
+    "void hl::gemm_splitk_reduce_norm<2>(float const*, int)",
+    GEMM.format(e=2),
+    GEMM.format(e=1),
+    "void hl::gemm_splitk_reduce<1>(float const*, int)",
+]
+# no split anywhere: no reduces, no merge, the second RMSNorm is a plain kernel
+PLAIN_CALL = [SPLIT_CALL[i] for i in (0, 1, 3, 4, 6, 0, 8, 9)]
+
+
+def test_split_call_fills_every_slot_in_order():
+    lab = SlotLabeler()
+    assert [lab.label(k) for k in SPLIT_CALL * 2] == list(SLOTS) * 2
+
+
+def test_unsplit_call_labels():
+    lab = SlotLabeler()
+    got = [lab.label(k) for k in PLAIN_CALL + SPLIT_CALL[:2]]
+    assert got == ["rmsnorm1", "gemm_qkv", "rope_kv_append", "attention", "gemm_o",
+                   "gemm_o_reduce_rmsnorm2", "gemm_gate_up", "gemm_down", "rmsnorm1", "gemm_qkv"]
+
+
+def test_foreign_kernels_are_skipped():
+    lab = SlotLabeler()
+    assert lab.label("__amd_rocclr_copyBuffer") is None
+    assert lab.label("void at::native::vectorized_elementwise_kernel<16>(int)") is None

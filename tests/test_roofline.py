@@ -34,13 +34,16 @@ def test_mistral_weight_bytes():
     s = rl.layer_stages(4096, 32, 8, 128, 14336, [256], [768], [1000] * 32)
     by = {x.name: x for x in s}
     w = (by["gemm_qkv"].bytes - 288 * 4096 * 2 - 288 * 6144 * 2
-         + by["gemm_o_rmsnorm2"].bytes - 288 * 4096 * 2 - 3 * 288 * 4096 * 2 - 4096 * 2
+         + by["gemm_o"].bytes - 288 * 4096 * 2 - 2 * 288 * 4096 * 2
          + by["gemm_gate_up"].bytes - 288 * 4096 * 2 - 288 * 14336 * 2
          + by["gemm_down"].bytes - 288 * 14336 * 2 - 2 * 288 * 4096 * 2)
     assert w == 2 * (6144 * 4096 + 4096 * 4096 + 2 * 14336 * 4096 + 4096 * 14336)
     prefill_bytes = (768 + 256) * MISTRAL_7B.kv_bytes_per_token + 2 * 256 * 4096 * 2
     decode_bytes = 32 * 1001 * MISTRAL_7B.kv_bytes_per_token + 2 * 32 * 4096 * 2
     assert by["attention"].bytes == prefill_bytes + decode_bytes
+    assert by["gemm_o_reduce_rmsnorm2"].bytes == 288 * 4096 * 2 + 4096 * 2
+    for k in ("gemm_qkv_reduce", "attention_merge", "gemm_down_reduce"):
+        assert by[k].bytes == 0 and by[k].flops == 0
     # below the ridge (~312 flop/B) the weight-streaming GEMMs are HBM-bound
     assert by["gemm_gate_up"].bound == "hbm"
     assert by["attention"].bound == "hbm"
