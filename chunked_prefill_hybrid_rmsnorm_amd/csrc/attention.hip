@@ -26,7 +26,9 @@
 namespace hl {
 
 constexpr int kAttnWaves = 4;
-constexpr int kPrefillRows = 16 * kAttnWaves;  // rows per prefill workgroup
+constexpr int kPfRowsPerWave = 32;                       // two 16-row MFMA blocks
+constexpr int kPrefillRows = kPfRowsPerWave * kAttnWaves;  // rows per prefill workgroup
+constexpr int kPfStages = 3;                             // LDS ring depth of prefill K/V
 
 struct AttnArgs {
   const bf16* qkv;
@@ -58,8 +60,74 @@ __device__ __forceinline__ void init_acc(AttnAcc<D>& a) {
   for (int i = 0; i < D / 16; ++i) a.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// K/V of one 32-key step staged in LDS for all waves of a prefill workgroup:
+// [K page 0 | K page 1 | V page 0 | V page 1], each 16 x D bf16.  Within a K
+// row the 16-byte chunks are permuted (chunk c at slot c ^ k_swz(row)) and
+// within a V row of 16 keys the two 8-key halves are swapped when
+// v_swz(dim) is set, so that every group of 8 lanes of a fragment read
+// touches 8 different 16-byte bank groups.
 template <int D>
-__device__ __forceinline__ void prefill_wave(const AttnArgs& A, int b, int wave, int l16, int q) {
+struct PfStage {
+  static constexpr int PAGE = 16 * D * 2;     // bytes of one page of one kv head
+  static constexpr int BYTES = 4 * PAGE;      // K and V of two pages
+  static constexpr int COPIES = BYTES / 1024;  // 1 KB copy instructions per step
+  static constexpr int PER_WAVE = COPIES / kAttnWaves;
+};
+
+__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+__device__ __forceinline__ int v_swz(int dim) { return (dim >> 2) & 1; }
+
+template <int D>
+__device__ __forceinline__ void prefill_copy(char* stage, const KvDev& kv, int g, int p0, int p1,
+                                             int wave, int lane) {
+  constexpr int PAGE = PfStage<D>::PAGE;
+#pragma unroll
+  for (int i = 0; i < PfStage<D>::PER_WAVE; ++i) {
+    const int ci = wave * PfStage<D>::PER_WAVE + i;  // 1 KB block of the stage
+    const int off = ci * 1024;                        // byte offset in the stage
+    const int region = off / PAGE;                    // 0, 1: K pages; 2, 3: V pages
+    const int page = (region & 1) ? p1 : p0;
+    const int in = off % PAGE + lane * 16;            // byte offset inside the page
+    const bf16* src;
+    if (region < 2) {
+      const int row = in / (D * 2), slot = (in % (D * 2)) / 16;
+      src = kv.k_page(page, g) + row * D + (slot ^ k_swz(row)) * 8;
+    } else {
+      const int dim = in / 32, half = (in % 32) / 16;
+      src = kv.v_page(page, g) + dim * 16 + (half ^ v_swz(dim)) * 8;
+    }
+    lds_dma16(src, stage + off);  // lane i fills bytes [16 i, 16 i + 16) of the block
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void prefill_frags(KvFrag<D>& f, const char* stage, int l16, int q) {
+  constexpr int PAGE = PfStage<D>::PAGE;
+#pragma unroll
+  for (int hp = 0; hp < 2; ++hp) {
+    const int key = step_key(hp, l16);
+    const int row = key & 15;
+    const char* kr = stage + (key >> 4) * PAGE + row * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) f.k[hp][ks] = ld16(kr + (((ks * 4 + q) ^ k_swz(row)) * 16));
+  }
+  const char* vb = stage + (2 + (q >> 1)) * PAGE;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    const int dim = db * 16 + l16;
+    f.v[db] = ld16(vb + dim * 32 + (((q & 1) ^ v_swz(dim)) * 16));
+  }
+}
+
+// A prefill workgroup: 128 GQA rows (row = token * G + head) of one chunk and
+// one kv head, 32 per wave as two 16-row MFMA blocks, over one key segment.
+// The waves copy each 32-key step's K/V pages into an LDS ring together
+// (global -> LDS, kPfStages deep) and all read it from there, so a K/V byte
+// crosses the L2 -> CU path once per 128 rows.
+template <int D>
+__device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave, int lane,
+                                              char* ring) {
+  const int l16 = lane & 15, q = lane >> 4;
   const int per_chunk = A.pf_gx * A.pf_ns * A.nkv;
   const int c = b / per_chunk;
   const int rem = b % per_chunk;
@@ -69,43 +137,88 @@ __device__ __forceinline__ void prefill_wave(const AttnArgs& A, int b, int wave,
   const ChunkDev ch = A.chunks.c[c];
   const int G = A.nq / A.nkv;
   const int rows_total = ch.len * G;
-  const int rbase = (rg * kAttnWaves + wave) * 16;
-  if (rbase >= rows_total) return;
+  const int wg_row0 = rg * kPrefillRows;
+  if (wg_row0 >= rows_total) return;  // whole workgroup idle (uniform)
   const int kv_len = ch.start_pos + ch.len;
-  const int ld = (A.nq + 2 * A.nkv) * D;
-
-  const int row = rbase + l16;
-  const bool valid = row < rows_total;
-  const int tok = valid ? row / G : 0;
-  const int hh = row % G;
-  const int row_limit = valid ? ch.start_pos + tok : -1;
-  bf16x8 qf[D / 32];
-  const bf16* qp = A.qkv + (size_t)(ch.row0 + tok) * ld + (size_t)(g * G + hh) * D;
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = valid ? as_bf16x8(ld16(qp + ks * 32 + q * 8)) : as_bf16x8(u32x4{0, 0, 0, 0});
-
-  const int last_row = min(rbase + 16, rows_total) - 1;
-  const int k_stop = ch.start_pos + last_row / G + 1;
+  const int wg_last = min(wg_row0 + kPrefillRows, rows_total) - 1;
+  const int k_stop = ch.start_pos + wg_last / G + 1;
   const int k0 = sp * A.pf_seg;
   const int k1 = min(k_stop, k0 + A.pf_seg);
-  if (k0 >= k1) return;  // none of this wave's rows reaches this segment
+  if (k0 >= k1) return;  // no row of the workgroup reaches this segment (uniform)
+  const int ld = (A.nq + 2 * A.nkv) * D;
 
-  AttnAcc<D> a;
-  init_acc<D>(a);
-  attend_segment<D>(a, qf, row_limit, k0, k1, kv_len, ch.block_table, ch.n_blocks, A.kv, g, l16, q);
-  const float l_tot = row_total(a.l);
-  if (!valid) return;
-  const int h = g * G + hh;
-  const int n_parts = min(A.pf_ns, (row_limit + A.pf_seg) / A.pf_seg);
-  if (sp >= n_parts) return;  // this row has no key in the segment
-  const int grow = ch.row0 + tok;
-  if (n_parts == 1) {
-    store_row<D>(a, l_tot, A.attn + (size_t)grow * A.nq * D + (size_t)h * D, q);
-    return;
+  // this wave's two row blocks
+  const int rbase = wg_row0 + wave * kPfRowsPerWave;
+  bf16x8 qf[2][D / 32];
+  int row_limit[2];
+  bool valid[2];
+  int tok[2], hh[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = rbase + rb * 16 + l16;
+    valid[rb] = row < rows_total;
+    tok[rb] = valid[rb] ? row / G : 0;
+    hh[rb] = row % G;
+    row_limit[rb] = valid[rb] ? ch.start_pos + tok[rb] : -1;
+    const bf16* qp = A.qkv + (size_t)(ch.row0 + tok[rb]) * ld + (size_t)(g * G + hh[rb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      qf[rb][ks] = valid[rb] ? as_bf16x8(ld16(qp + ks * 32 + q * 8))
+                             : as_bf16x8(u32x4{0, 0, 0, 0});
   }
-  const size_t pidx = ((size_t)grow * A.nq + h) * A.pf_ns + sp;
-  store_partial<D>(a, l_tot, A.pf_o + pidx * D, A.pf_ml + pidx * 2, q);
+  const bool busy = rbase < rows_total;  // wave has rows (still copies and syncs if not)
+  const int lim_min[2] = {wave_min(row_limit[0]), wave_min(row_limit[1])};
+
+  const int blk_end = (k1 + 15) >> 4;
+  PageWindow win;
+  win.fill(ch.block_table, ch.n_blocks, k0 >> 4, blk_end, A.kv.num_pages, lane);
+  const int nsteps = (k1 - k0 + 31) / 32;
+  // keys from block blk_end on are read from a stand-in page: zero their V
+  const int v_end = min(kv_len, blk_end * 16);
+  // copies of step s (clamped to the last step; pages past the table read page
+  // 0, whose keys are masked) so every wave issues the same count each step
+  auto issue = [&](int s) {
+    const int t = k0 + min(s, nsteps - 1) * 32;
+    int p0 = win.at(t, ch.block_table, ch.n_blocks, blk_end, A.kv.num_pages, lane);
+    int p1 = win.at(t + 16, ch.block_table, ch.n_blocks, blk_end, A.kv.num_pages, lane);
+    prefill_copy<D>(ring + (s % kPfStages) * PfStage<D>::BYTES, A.kv, g, max(p0, 0), max(p1, 0),
+                    wave, lane);
+  };
+
+  AttnAcc<D> a[2];
+  init_acc<D>(a[0]);
+  init_acc<D>(a[1]);
+  const float scale = kAttnLog2e * rsqrtf((float)D);
+#pragma unroll
+  for (int s = 0; s < kPfStages - 1; ++s) issue(s);
+  for (int i = 0; i < nsteps; ++i) {
+    wait_vmcnt<PfStage<D>::PER_WAVE * (kPfStages - 2)>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(i + kPfStages - 1);
+    if (!busy) continue;
+    KvFrag<D> f;
+    prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
+    const int t0 = k0 + i * 32;
+    compute_step<D, 2>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale, q);
+  }
+  wait_vmcnt<0>();  // the clamped tail copies land before the workgroup ends
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float l_tot = row_total(a[rb].l);
+    if (!valid[rb]) continue;
+    const int h = g * G + hh[rb];
+    const int n_parts = min(A.pf_ns, (row_limit[rb] + A.pf_seg) / A.pf_seg);
+    if (sp >= n_parts) continue;  // this row has no key in the segment
+    const int grow = ch.row0 + tok[rb];
+    if (n_parts == 1) {
+      store_row<D>(a[rb], l_tot, A.attn + (size_t)grow * A.nq * D + (size_t)h * D, q);
+      continue;
+    }
+    const size_t pidx = ((size_t)grow * A.nq + h) * A.pf_ns + sp;
+    store_partial<D>(a[rb], l_tot, A.pf_o + pidx * D, A.pf_ml + pidx * 2, q);
+  }
 }
 
 template <int D>
@@ -149,11 +262,12 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int l16
 
 template <int D>
 __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) {
+  __shared__ __attribute__((aligned(1024))) char ring[kPfStages * PfStage<D>::BYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q = lane >> 4;
   const int b = blockIdx.x;
   if (b < A.pf_wgs)
-    prefill_wave<D>(A, b, wave, l16, q);
+    prefill_block<D>(A, b, wave, lane, ring);
   else
     decode_wave<D>(A, (b - A.pf_wgs) * kAttnWaves + wave, l16, q);
 }

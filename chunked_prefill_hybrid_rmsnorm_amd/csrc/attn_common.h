@@ -10,12 +10,39 @@
 // online in base 2.  Keys are visited 32 at a time (two pages); page ids come
 // from a register window of the block table and the next step's K/V
 // fragments are loaded while the current step is multiplied.
+//
+// Key order inside a 32-key step: S^T is computed as two 16-row blocks hp,
+// and row r of block hp holds key kappa(hp, r) = 8 (r / 4) + 4 hp + r % 4.  Lane
+// (l16, q) then receives keys 8q .. 8q + 7 (four from each block), which are
+// 8 consecutive keys of one page: its P values are the B operand of the second
+// product in key order, and its V^T operand is one 16-byte piece of the page.
 #pragma once
 #include "kernels.h"
 
 namespace hl {
 
 constexpr float kAttnLog2e = 1.4426950408889634f;
+
+// key (0..31 inside the step) held by S^T row r of block hp
+__device__ __forceinline__ int step_key(int hp, int r) { return 8 * (r >> 2) + 4 * hp + (r & 3); }
+
+// max / sum over the four lanes l16, l16 + 16, l16 + 32, l16 + 48 (one row)
+__device__ __forceinline__ float quad_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x with the hardware instruction (results below 2^-126 flush to 0, which
+// only drops probabilities that cannot change an fp32 sum)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int D>
 struct AttnAcc {
@@ -25,86 +52,138 @@ struct AttnAcc {
 
 template <int D>
 struct KvFrag {
-  u32x4 k[2][D / 32];  // two pages, K rows (16 B per lane per k-step)
-  u32x2 v[2][D / 16];  // two pages, V^T pieces (8 B per lane per dim block)
+  u32x4 k[2][D / 32];  // K rows of keys kappa(hp, l16), 16 B per lane per k-step
+  u32x4 v[D / 16];     // V^T of keys 8q .. 8q + 7 for dims 16 db + l16
 };
 
+// Step fragments straight from the pages (decode); page -1 reads as zeros.
 template <int D>
 __device__ __forceinline__ void load_step(KvFrag<D>& f, const KvDev& kv, int g, int p0, int p1,
                                           int l16, int q) {
-  const int pg[2] = {p0, p1};
 #pragma unroll
   for (int hp = 0; hp < 2; ++hp) {
-    const bf16* kp = pg[hp] >= 0 ? kv.k_page(pg[hp], g) : nullptr;
-    const bf16* vp = pg[hp] >= 0 ? kv.v_page(pg[hp], g) : nullptr;
+    const int key = step_key(hp, l16);
+    const int pg = key < 16 ? p0 : p1;
+    const bf16* kp = pg >= 0 ? kv.k_page(pg, g) + (key & 15) * D : nullptr;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      f.k[hp][ks] = kp ? ld16(kp + l16 * D + ks * 32 + q * 8) : u32x4{0, 0, 0, 0};
+      f.k[hp][ks] = kp ? ld16(kp + ks * 32 + q * 8) : u32x4{0, 0, 0, 0};
+  }
+  const int pv = q < 2 ? p0 : p1;
+  const bf16* vp = pv >= 0 ? kv.v_page(pv, g) + (q & 1) * 8 : nullptr;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      f.v[hp][db] = vp ? ld8(vp + (db * 16 + l16) * 16 + 4 * q) : u32x2{0, 0};
+  for (int db = 0; db < D / 16; ++db)
+    f.v[db] = vp ? ld16(vp + (db * 16 + l16) * 16) : u32x4{0, 0, 0, 0};
+}
+
+// Largest growth of the running max (base-2 units) that is not folded into
+// the accumulators at once: while a new max stays within kRescaleSlack of the
+// one in use, probabilities are taken against the old max (they stay below
+// 2^kRescaleSlack, exact in fp32 and bf16 range) and the O / l rescale is
+// skipped.  The final o / l does not depend on which max was used.
+constexpr float kRescaleSlack = 8.f;
+
+// Multiply one 32-key step starting at t0 for NRB 16-row blocks sharing the
+// step's K/V fragments.  Key t counts for a lane's row iff t <= row_limit
+// (causal / context bound) and t < k_end (segment end); keys >= v_end have no
+// valid V (past the request, or a stand-in page) and are zeroed before the
+// product.  `lim_min[rb]` is the smallest row_limit over the wave's rows of
+// block rb: a step below it and below v_end needs no masking at all.
+template <int D, int NRB>
+__device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<D>& f,
+                                             const bf16x8 (&qf)[NRB][D / 32], int t0,
+                                             const int (&row_limit)[NRB],
+                                             const int (&lim_min)[NRB], int k_end, int v_end,
+                                             float scale, int q) {
+  const bool v_full = t0 + 31 < v_end;
+  uint32_t vm[4];  // keep-masks of this lane's V keys t0 + 8q + 2w, + 1
+  if (!v_full) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int t = t0 + 8 * q + 2 * w;
+      vm[w] = (t < v_end ? 0x0000ffffu : 0u) | (t + 1 < v_end ? 0xffff0000u : 0u);
+    }
+  }
+  f32x4 s[NRB][2];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+      s[rb][hp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        s[rb][hp] = mfma16x16x32(as_bf16x8(f.k[hp][ks]), qf[rb][ks], s[rb][hp]);
+    }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    AttnAcc<D>& acc = a[rb];
+    const bool full = t0 + 31 <= min(lim_min[rb], k_end - 1);  // wave-uniform
+    float smax = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[rb][hp][r] *= scale;
+          smax = fmaxf(smax, s[rb][hp][r]);
+        }
+    } else {
+      const int lim = min(row_limit[rb], k_end - 1);
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 8 * q + 4 * hp + r;
+          s[rb][hp][r] = t <= lim ? s[rb][hp][r] * scale : -INFINITY;
+          smax = fmaxf(smax, s[rb][hp][r]);
+        }
+    }
+    smax = quad_max(smax);
+    // move the max in use only when the new one is well above it; a row with
+    // no visible key so far keeps m = -inf and uses 0 as its shift, so that
+    // no -inf - -inf appears (its probabilities are exactly 0)
+    const bool grow = smax > acc.m + kRescaleSlack;
+    if (__any(grow)) {
+      const float m_next = grow ? smax : acc.m;
+      const float alpha = grow ? fast_exp2(acc.m - m_next) : 1.f;  // 2^-inf = 0 on the first key
+      acc.m = m_next;
+      acc.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) acc.o[db] *= alpha;
+    }
+    const float m_use = acc.m == -INFINITY ? 0.f : acc.m;
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = fast_exp2(s[rb][hp][r] - m_use);
+        psum += p[r];
+      }
+      pk[hp * 2 + 0] = pack2(p[0], p[1]);
+      pk[hp * 2 + 1] = pack2(p[2], p[3]);
+    }
+    acc.l += psum;
+    const bf16x8 pf = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      u32x4 va = f.v[db];
+      if (!v_full) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) va[w] &= vm[w];
+      }
+      acc.o[db] = mfma16x16x32(as_bf16x8(va), pf, acc.o[db]);
+    }
   }
 }
 
-// Multiply one 32-key step starting at t0.  Key t counts for this lane's row
-// iff t <= row_limit (causal / context bound) and t < k_end (segment end);
-// keys >= kv_len hold no token, so their V is zeroed before the product.
-template <int D>
-__device__ __forceinline__ void compute_step(AttnAcc<D>& a, const KvFrag<D>& f,
-                                             const bf16x8 (&qf)[D / 32], int t0, int row_limit,
-                                             int k_end, int kv_len, float scale, int q) {
-  const int lim = min(row_limit, k_end - 1);
-  f32x4 s[2];
-  float smax = -INFINITY;
+// Smallest value of v over the wave.
+__device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
-  for (int hp = 0; hp < 2; ++hp) {
-    s[hp] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) s[hp] = mfma16x16x32(as_bf16x8(f.k[hp][ks]), qf[ks], s[hp]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + hp * 16 + 4 * q + r;
-      s[hp][r] = t <= lim ? s[hp][r] * scale : -INFINITY;
-      smax = fmaxf(smax, s[hp][r]);
-    }
-  }
-  smax = fmaxf(smax, __shfl_xor(smax, 16));
-  smax = fmaxf(smax, __shfl_xor(smax, 32));
-  const float m_new = fmaxf(a.m, smax);
-  // a row with no visible key so far keeps m = -inf: use 0 as the shift so
-  // that no -inf - -inf appears; its probabilities are exactly 0
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = exp2f(a.m - m_use);
-  a.m = m_new;
-  float psum = 0.f;
-  uint32_t pk[4];
-#pragma unroll
-  for (int hp = 0; hp < 2; ++hp) {
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = exp2f(s[hp][r] - m_use);
-      psum += p[r];
-    }
-    pk[hp * 2 + 0] = pack2(p[0], p[1]);
-    pk[hp * 2 + 1] = pack2(p[2], p[3]);
-  }
-  a.l = a.l * alpha + psum;
-  const bf16x8 pf = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-  uint32_t vm[2][2];
-#pragma unroll
-  for (int hp = 0; hp < 2; ++hp) {
-    const int t = t0 + hp * 16 + 4 * q;
-    vm[hp][0] = (t + 0 < kv_len ? 0x0000ffffu : 0u) | (t + 1 < kv_len ? 0xffff0000u : 0u);
-    vm[hp][1] = (t + 2 < kv_len ? 0x0000ffffu : 0u) | (t + 3 < kv_len ? 0xffff0000u : 0u);
-  }
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    a.o[db] *= alpha;
-    const u32x4 va = {f.v[0][db][0] & vm[0][0], f.v[0][db][1] & vm[0][1],
-                      f.v[1][db][0] & vm[1][0], f.v[1][db][1] & vm[1][1]};
-    a.o[db] = mfma16x16x32(as_bf16x8(va), pf, a.o[db]);
-  }
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
 }
 
 // A wave's window of 64 consecutive block-table entries (lane i holds the page
@@ -147,6 +226,12 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
     p0 = win.at(t, bt, n_blocks, blk_end, kv.num_pages, lane);
     p1 = win.at(t + 16, bt, n_blocks, blk_end, kv.num_pages, lane);
   };
+  AttnAcc<D> ab[1] = {a};
+  bf16x8 qb[1][D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) qb[0][ks] = qf[ks];
+  const int rl[1] = {row_limit};
+  const int lm[1] = {wave_min(row_limit)};
   KvFrag<D> fa, fb;
   int p0, p1;
   pages(k0, p0, p1);
@@ -159,24 +244,22 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
       pages(t1, p0, p1);
       load_step<D>(fb, kv, g, p0, p1, l16, q);
     }
-    compute_step<D>(a, fa, qf, t0, row_limit, k1, kv_len, scale, q);
+    compute_step<D, 1>(ab, fa, qb, t0, rl, lm, k1, kv_len, scale, q);
     if (t1 >= k1) break;
     const int t2 = t1 + 32;
     if (t2 < k1) {
       pages(t2, p0, p1);
       load_step<D>(fa, kv, g, p0, p1, l16, q);
     }
-    compute_step<D>(a, fb, qf, t1, row_limit, k1, kv_len, scale, q);
+    compute_step<D, 1>(ab, fb, qb, t1, rl, lm, k1, kv_len, scale, q);
     if (t2 >= k1) break;
     t0 = t2;
   }
+  a = ab[0];
 }
 
 // Sum of l over the four lanes holding one row.
-__device__ __forceinline__ float row_total(float l) {
-  l += __shfl_xor(l, 16);
-  return l + __shfl_xor(l, 32);
-}
+__device__ __forceinline__ float row_total(float l) { return quad_sum(l); }
 
 // Final bf16 output of one row: lane writes dims 16 db + 4q .. + 4.
 template <int D>

@@ -27,8 +27,11 @@ __device__ __forceinline__ bf16 f2bf(float f) {
   return __builtin_bit_cast(bf16, h);
 }
 
+// two fp32 -> two bf16 (round to nearest even) in one 32-bit word, a low
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // D = A(16x32) * B(32x16) + C.  Lane l supplies A[l%16][8*(l/16) .. +8] and
@@ -51,6 +54,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): `lds` is the
+// wave-uniform base and lane i's bytes land at lds + 16 i, no registers involved.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter: wait until at most n remain.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Chunk descriptors passed by value to kernels.

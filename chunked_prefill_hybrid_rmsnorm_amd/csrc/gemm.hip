@@ -150,7 +150,13 @@ template <int EPI>
 static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2,
                              bf16* c, const bf16* r, float* part, int m, int mp, int n, int k,
                              hipStream_t s) {
-  if (ch.big) return run_gemm_dma<288, 128, 2, 4, EPI, 3>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  if (ch.big) {
+    // long k loops amortise the k-group reduction: 4 waves per group, each
+    // with a 144 x 64 sub-tile (fewer LDS bytes per MFMA)
+    if ((k / kGemmBK) / ch.splits >= 48)
+      return run_gemm_dma<288, 128, 2, 2, EPI, 3, 64, 2>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+    return run_gemm_dma<288, 128, 2, 4, EPI, 3>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  }
   return run_gemm_dma<128, 128, 2, 2, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
 }
 

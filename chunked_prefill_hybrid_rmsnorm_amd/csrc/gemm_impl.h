@@ -17,25 +17,18 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 // bank conflicts.  Wave w issues blocks w, w + NW, ...  Rows past the end of
 // A or W are clamped to the last valid row: their products only reach
 // outputs that are never stored.
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds, 16, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory counter: wait until at most n remain.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <int BK>
 __device__ __forceinline__ int swz(int row, int chunk) {
   return BK == 64 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 2) & 3));
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
+// KG > 1 splits each k-step between KG groups of WM x WN waves (group g
+// multiplies the g-th 32-wide slice of every stage): every wave keeps a large
+// sub-tile, so fewer LDS bytes are read per MFMA, while the workgroup still
+// holds two waves per SIMD.  The groups' partial tiles are summed through LDS
+// at the end, each group finishing half of the row fragments.
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1>
+__global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W2,
     bf16* __restrict__ C, const bf16* __restrict__ R, float* __restrict__ part, int M, int Mp,
     int N, int K, int n_mtiles, int n_ntiles, int splits) {
@@ -43,7 +36,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
   constexpr int ROWB = BK * 2;            // bytes of one tile row in a stage
   constexpr int BLK_ROWS = 1024 / ROWB;   // rows per 1 KB copy block
   constexpr int NCH = BK / 8;             // 16-byte chunks per row
-  constexpr int NW = WM * WN;  // waves in the workgroup
+  constexpr int NWG = WM * WN;  // waves per k-group
+  constexpr int NW = NWG * KG;  // waves in the workgroup
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
@@ -58,6 +52,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
   static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && (BN / 2) % BLK_ROWS == 0), "swiglu pairing");
   static_assert(STAGES >= 3, "need at least three stages");
   static_assert(PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(KG == 1 || KG == BK / 32, "a k-group takes one 32-wide slice of a stage");
+  static_assert(KG == 1 || NWG * FM * FN * 1024 <= STAGES * STAGE_BYTES, "reduction fits the ring");
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -80,7 +76,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int kg = wave / NWG, wl = wave % NWG;
+  const int wm = wl / WN, wn = wl % WN;
   const int l16 = lane & 15, q = lane >> 4;
 
   // per-lane source row pointers of this wave's copy blocks (k offset added per stage)
@@ -159,7 +156,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
       issue(it + STAGES - 1);
       const char* st = smem + (it % STAGES) * STAGE_BYTES;
 #pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) {
+      for (int kk = 0; kk < BK / 32 / KG; ++kk) {
+        const int ks = kk * KG + kg;
         bf16x8 af[FN], bfr[FM];
         const int so = swz<BK>(l16, ks * 4 + q) << 4;
 #pragma unroll
@@ -174,8 +172,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     }
   }
   wait_vmcnt<0>();  // drain the clamped tail copies before the workgroup ends
+  // k-groups: group 0 finishes row fragments [0, FSPLIT), group 1 the rest;
+  // each hands the other group's share to its partner wave through LDS
+  constexpr int FSPLIT = (FM + 1) / 2;
+  if (KG > 1) {
+    __syncthreads();  // every wave is done with the ring and every copy has landed
+    f32x4* red = reinterpret_cast<f32x4*>(smem) + (size_t)wl * FM * FN * 64;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if ((fm < FSPLIT) == (kg == 0)) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) red[(fm * FN + fn) * 64 + lane] = acc[fn][fm];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if ((fm < FSPLIT) != (kg == 0)) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const f32x4 o = red[(fm * FN + fn) * 64 + lane];
+        acc[fn][fm] += o;
+      }
+    }
+  }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
+    if (KG > 1 && (fm < FSPLIT) != (kg == 0)) continue;
     const int m = m0 + wm * WTM + fm * 16 + l16;
     if (splits > 1) {
       if (m >= Mp) continue;
@@ -223,7 +245,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64>
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1>
 hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, const bf16* r,
                         float* part, int m, int mp, int n, int k, int splits, hipStream_t s) {
   constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
@@ -231,12 +253,12 @@ hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, c
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int mt = (mp + BM - 1) / BM, nt = (n + OUT_N - 1) / OUT_N;
   if (EPI == EPI_SWIGLU) splits = 1;
-  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK>;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK, KG>;
   // raise the dynamic LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(mt * nt * splits), dim3(64 * WM * WN), lds, s, a, w, w2, c, r, part,
+  hipLaunchKernelGGL(kern, dim3(mt * nt * splits), dim3(64 * WM * WN * KG), lds, s, a, w, w2, c, r, part,
                      m, mp, n, k, mt, nt, splits);
   return hipGetLastError();
 }

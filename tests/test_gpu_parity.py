@@ -67,9 +67,15 @@ def test_rmsnorm_step():
     assert np.all(got[37:] == 0)
 
 
-@pytest.mark.parametrize("m,mp,n,k", [(68, 80, 512, 256), (288, 288, 6144, 4096),
-                                      (1, 16, 256, 1024), (257, 272, 4096, 14336)])
-def test_gemm_step(m, mp, n, k):
+@pytest.mark.parametrize("m,mp,n,k,split", [(68, 80, 512, 256, False),
+                                            (288, 288, 6144, 4096, False),
+                                            (288, 288, 6144, 4096, True),
+                                            (1, 16, 256, 1024, False),
+                                            (257, 272, 4096, 14336, False),
+                                            (257, 272, 4096, 14336, True)])
+def test_gemm_step(m, mp, n, k, split):
+    """Without a workspace K is not split (one launch, the long-k tile with two
+    k-groups for the 288-row shapes); with one the partials are reduced."""
     import torch
     rng = np.random.default_rng(m + n)
     a = np.zeros((mp, k), np.uint16)
@@ -77,10 +83,15 @@ def test_gemm_step(m, mp, n, k):
     w = bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
     r = bf16_bits(rng.standard_normal((m, n)).astype(np.float32))
     ad, wd, rd = B.bits_to_device(a), B.bits_to_device(w), B.bits_to_device(r)
+    ws, nbytes = None, 0
+    if split:
+        nbytes = B.hl_gemm_workspace_bytes(mp, n, k)
+        assert nbytes > 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     c = torch.empty((mp, n), dtype=torch.bfloat16, device="cuda")
-    B.hl_gemm_bf16(ad, wd, c, None, m, mp, n, k)
+    B.hl_gemm_bf16(ad, wd, c, None, m, mp, n, k, ws, nbytes)
     c2 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-    B.hl_gemm_bf16(ad, wd, c2, rd, m, mp, n, k)
+    B.hl_gemm_bf16(ad, wd, c2, rd, m, mp, n, k, ws, nbytes)
     torch.cuda.synchronize()
     ref = widen(a) @ widen(w).T
     got = tap_f64(c, mp)
@@ -89,10 +100,10 @@ def test_gemm_step(m, mp, n, k):
     assert_close("gemm+residual", tap_f64(c2, m), ref[:m] + widen(r))
 
 
-def test_swiglu_step():
+@pytest.mark.parametrize("mp,f,k", [(96, 1024, 512), (272, 1024, 4096)])
+def test_swiglu_step(mp, f, k):
     import torch
     rng = np.random.default_rng(5)
-    mp, f, k = 96, 1024, 512
     a = bf16_bits(rng.standard_normal((mp, k)).astype(np.float32))
     wg = bf16_bits((rng.standard_normal((f, k)) * 0.05).astype(np.float32))
     wu = bf16_bits((rng.standard_normal((f, k)) * 0.05).astype(np.float32))
