@@ -28,7 +28,7 @@ int check_config(const hl_config* c) {
 
 struct Layout {
   int Mp;
-  size_t pos, slot, xn1, qkv, attn, h, xn2, act, dec, pre, gemm, total;
+  size_t pos, slot, cs, sn, xn1, qkv, attn, h, xn2, act, dec, pre, gemm, total;
 };
 
 Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad) {
@@ -40,6 +40,8 @@ Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad
   size_t o = 0;
   L.pos = o;  o = align256(o + Mp * 4);
   L.slot = o; o = align256(o + Mp * 4);
+  L.cs = o;   o = align256(o + Mp * (d / 2) * 4);
+  L.sn = o;   o = align256(o + Mp * (d / 2) * 4);
   L.xn1 = o;  o = align256(o + Mp * H * 2);
   L.qkv = o;  o = align256(o + Mp * nqkv * 2);
   L.attn = o; o = align256(o + Mp * c->n_q_heads * d * 2);
@@ -130,9 +132,9 @@ int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t m
 }
 
 static const char* const kStageNames[HL_N_STAGES] = {
-    "rmsnorm1",       "gemm_qkv",  "gemm_qkv_reduce",    "rope_kv_append",
-    "attention",      "attention_merge", "gemm_o",      "gemm_o_reduce_rmsnorm2",
-    "gemm_gate_up",   "gemm_down", "gemm_down_reduce"};
+    "rmsnorm1",  "gemm_qkv",       "rope_kv_append",         "attention",
+    "attention_merge", "gemm_o",  "gemm_o_reduce_rmsnorm2", "gemm_gate_up",
+    "gemm_down", "gemm_down_reduce"};
 
 const char* hl_stage_name(int stage) {
   return (stage >= 0 && stage < HL_N_STAGES) ? kStageNames[stage] : "";
@@ -201,17 +203,27 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
     if (!mark()) return HL_ERR_HIP; \
   } while (0)
   HL_MARK();
-  // RMSNorm of the input rows (pad rows -> 0)
-  HL_TRY(launch_rmsnorm(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
-                        cfg->rms_eps, stream));
+  // RMSNorm of the input rows (pad rows -> 0); each row's position, KV slot
+  // and RoPE cos / sin go to a table for the append step
+  const RopeTab tab{reinterpret_cast<int32_t*>(base + L.pos), reinterpret_cast<int32_t*>(base + L.slot),
+                    reinterpret_cast<float*>(base + L.cs), reinterpret_cast<float*>(base + L.sn)};
+  HL_TRY(launch_rmsnorm_rope_table(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
+                                   cfg->rms_eps, cl, dd, kvd, d, cfg->rope_theta, tab, stream));
   HL_MARK();
-  // fused QKV projection on the stacked rows, then the split-K reduce
+  // fused QKV projection on the stacked rows; with split K its partials are
+  // summed by the RoPE / append kernel that follows
   void* gws = base + L.gemm;
-  HL_TRY(launch_gemm(EPI_STORE, xn1, reinterpret_cast<const bf16*>(w->w_qkv), nullptr, qkv,
-                     nullptr, gws, M, Mp, nqkv, H, stream, mid()));
+  const int qkv_splits = gemm_splits(EPI_STORE, Mp, nqkv, H);
+  if (qkv_splits > 1)
+    HL_TRY(launch_gemm_partials(xn1, reinterpret_cast<const bf16*>(w->w_qkv), gws, M, Mp, nqkv, H,
+                                stream));
+  else
+    HL_TRY(launch_gemm(EPI_STORE, xn1, reinterpret_cast<const bf16*>(w->w_qkv), nullptr, qkv,
+                       nullptr, gws, M, Mp, nqkv, H, stream));
   HL_MARK();
   // each row's position and KV slot, RoPE on q and k, append K and V
-  HL_TRY(launch_rope_kv_append_meta(qkv, cl, dd, nq, nkv, d, cfg->rope_theta, kvd, stream));
+  HL_TRY(launch_rope_append_wide(qkv, qkv_splits > 1 ? reinterpret_cast<const float*>(gws) : nullptr,
+                                 qkv_splits, M, Mp, nq, nkv, d, kvd, tab, stream));
   HL_MARK();
   // chunk-prefill attention (rows [0, Lp)) and paged decode attention
   // (rows [Lp, M)) in one launch

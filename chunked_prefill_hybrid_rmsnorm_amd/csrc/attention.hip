@@ -221,6 +221,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   }
 }
 
+static_assert(kDecodePart % 32 == 0 && kDecodePart <= 64 * 16,
+              "a decode unit is whole steps and fits one block-table window");
+
 template <int D>
 __device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int l16, int q) {
   // unit = ((j * parts + part) * nkv + g): a workgroup's waves share (j, part)
@@ -263,7 +266,10 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int l16
 template <int D>
 __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(1024))) char ring[kPfStages * PfStage<D>::BYTES];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave: keep it (and everything derived
+  // from it: work unit, key range, loop bounds) in scalar registers, so that
+  // the loops branch on scalars instead of masking lanes
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, q = lane >> 4;
   const int b = blockIdx.x;
   if (b < A.pf_wgs)

@@ -56,7 +56,11 @@ struct KvFrag {
   u32x4 v[D / 16];     // V^T of keys 8q .. 8q + 7 for dims 16 db + l16
 };
 
-// Step fragments straight from the pages (decode); page -1 reads as zeros.
+// Step fragments straight from the pages (decode).  A missing page (-1, past
+// the block table or the segment) reads page 0 instead: its keys are past
+// the segment end, so their scores are masked, and their V is zeroed through
+// v_end (see attend_segment).  Nothing here looks at the loaded values, so
+// the loads stay in flight while the previous step is multiplied.
 template <int D>
 __device__ __forceinline__ void load_step(KvFrag<D>& f, const KvDev& kv, int g, int p0, int p1,
                                           int l16, int q) {
@@ -64,16 +68,14 @@ __device__ __forceinline__ void load_step(KvFrag<D>& f, const KvDev& kv, int g, 
   for (int hp = 0; hp < 2; ++hp) {
     const int key = step_key(hp, l16);
     const int pg = key < 16 ? p0 : p1;
-    const bf16* kp = pg >= 0 ? kv.k_page(pg, g) + (key & 15) * D : nullptr;
+    const bf16* kp = kv.k_page(max(pg, 0), g) + (key & 15) * D + q * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      f.k[hp][ks] = kp ? ld16(kp + ks * 32 + q * 8) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < D / 32; ++ks) f.k[hp][ks] = ld16(kp + ks * 32);
   }
   const int pv = q < 2 ? p0 : p1;
-  const bf16* vp = pv >= 0 ? kv.v_page(pv, g) + (q & 1) * 8 : nullptr;
+  const bf16* vp = kv.v_page(max(pv, 0), g) + (q & 1) * 8 + l16 * 16;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    f.v[db] = vp ? ld16(vp + (db * 16 + l16) * 16) : u32x4{0, 0, 0, 0};
+  for (int db = 0; db < D / 16; ++db) f.v[db] = ld16(vp + db * 256);
 }
 
 // Largest growth of the running max (base-2 units) that is not folded into
@@ -210,7 +212,11 @@ struct PageWindow {
   }
 };
 
-// Keys [k0, k1) (k0 a multiple of 32) of one request through its block table.
+// Keys [k0, k1) of one decode (k0 a multiple of 32, at most 64 blocks, so one
+// block-table window covers them) through its block table.  Every step loads
+// its fragments one step ahead, and every half of the loop issues exactly one
+// step's loads (the last one repeats the final step), so the wait before a
+// multiply covers only the loads of that step.
 template <int D>
 __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)[D / 32],
                                                int row_limit, int k0, int k1, int kv_len,
@@ -219,12 +225,15 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
   const float scale = kAttnLog2e * rsqrtf((float)D);
   if (k0 >= k1) return;
   const int lane = l16 + 16 * q;
-  const int blk_end = (k1 + 15) >> 4;
+  const int blk0 = k0 >> 4, blk_end = (k1 + 15) >> 4;
   PageWindow win;
-  win.fill(bt, n_blocks, k0 >> 4, blk_end, kv.num_pages, lane);
-  auto pages = [&](int t, int& p0, int& p1) {
-    p0 = win.at(t, bt, n_blocks, blk_end, kv.num_pages, lane);
-    p1 = win.at(t + 16, bt, n_blocks, blk_end, kv.num_pages, lane);
+  win.fill(bt, n_blocks, blk0, blk_end, kv.num_pages, lane);
+  const int nst = (k1 - k0 + 31) / 32;
+  auto load = [&](KvFrag<D>& f, int st) {  // step st, clamped to the last one
+    const int b = blk0 + 2 * min(st, nst - 1);
+    const int p0 = b < blk_end ? __builtin_amdgcn_readlane(win.page, b - blk0) : -1;
+    const int p1 = b + 1 < blk_end ? __builtin_amdgcn_readlane(win.page, b + 1 - blk0) : -1;
+    load_step<D>(f, kv, g, p0, p1, l16, q);
   };
   AttnAcc<D> ab[1] = {a};
   bf16x8 qb[1][D / 32];
@@ -232,28 +241,16 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
   for (int ks = 0; ks < D / 32; ++ks) qb[0][ks] = qf[ks];
   const int rl[1] = {row_limit};
   const int lm[1] = {wave_min(row_limit)};
+  // keys from block blk_end on come from a stand-in page: zero their V
+  const int v_end = min(kv_len, blk_end * 16);
+  // an odd step count gets one more step past k1: all its keys are masked
   KvFrag<D> fa, fb;
-  int p0, p1;
-  pages(k0, p0, p1);
-  load_step<D>(fa, kv, g, p0, p1, l16, q);
-  int t0 = k0;
-  while (true) {
-    // fa holds step t0; fetch t0 + 32 into fb, then multiply fa
-    const int t1 = t0 + 32;
-    if (t1 < k1) {
-      pages(t1, p0, p1);
-      load_step<D>(fb, kv, g, p0, p1, l16, q);
-    }
-    compute_step<D, 1>(ab, fa, qb, t0, rl, lm, k1, kv_len, scale, q);
-    if (t1 >= k1) break;
-    const int t2 = t1 + 32;
-    if (t2 < k1) {
-      pages(t2, p0, p1);
-      load_step<D>(fa, kv, g, p0, p1, l16, q);
-    }
-    compute_step<D, 1>(ab, fb, qb, t1, rl, lm, k1, kv_len, scale, q);
-    if (t2 >= k1) break;
-    t0 = t2;
+  load(fa, 0);
+  for (int i = 0; i < nst; i += 2) {
+    load(fb, i + 1);
+    compute_step<D, 1>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
+    load(fa, i + 2);
+    compute_step<D, 1>(ab, fb, qb, k0 + 32 * (i + 1), rl, lm, k1, v_end, scale, q);
   }
   a = ab[0];
 }

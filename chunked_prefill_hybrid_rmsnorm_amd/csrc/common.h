@@ -17,7 +17,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 // Tokens per decode-attention partition (split-K unit).
-constexpr int kDecodePart = 256;
+#ifndef HL_DECODE_PART
+#define HL_DECODE_PART 256
+#endif
+constexpr int kDecodePart = HL_DECODE_PART;  // keys per decode work unit
 
 __device__ __forceinline__ float bf2f(bf16 b) { return __uint_as_float((uint32_t)b << 16); }
 

@@ -141,6 +141,8 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   return c;
 }
 
+int gemm_splits(GemmEpilogue epi, int mp, int n, int k) { return choose(epi, mp, n, k).splits; }
+
 size_t gemm_workspace_bytes(GemmEpilogue epi, int mp, int n, int k) {
   const Choice c = choose(epi, mp, n, k);
   return c.splits > 1 ? (size_t)c.splits * mp * n * sizeof(float) : 0;
@@ -158,6 +160,15 @@ static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, con
     return run_gemm_dma<288, 128, 2, 4, EPI, 3>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
   }
   return run_gemm_dma<128, 128, 2, 2, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+}
+
+hipError_t launch_gemm_partials(const bf16* a, const bf16* w, void* ws, int m, int mp, int n, int k,
+                                hipStream_t s) {
+  if (mp == 0 || n == 0) return hipSuccess;
+  const Choice ch = choose(EPI_STORE, mp, n, k);
+  if (ch.splits <= 1 || ws == nullptr) return hipErrorInvalidValue;
+  return run_choice<EPI_STORE>(ch, a, w, nullptr, nullptr, nullptr, reinterpret_cast<float*>(ws),
+                               m, mp, n, k, s);
 }
 
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,

@@ -28,6 +28,12 @@ size_t gemm_workspace_bytes(GemmEpilogue epi, int m_padded, int n, int k);
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
                        const bf16* residual, void* ws, int m, int m_padded, int n, int k,
                        hipStream_t s, hipEvent_t mid = nullptr);
+// K splits launch_gemm would use for this shape with a workspace
+int gemm_splits(GemmEpilogue epi, int m_padded, int n, int k);
+// Plain-store GEMM that leaves its split-K partials in ws for a consumer that
+// reduces them itself (gemm_splits(...) > 1 planes of [m_padded][n] fp32)
+hipError_t launch_gemm_partials(const bf16* a, const bf16* w, void* ws, int m, int m_padded, int n,
+                                int k, hipStream_t s);
 
 // h = a w^T + residual (rows < m) followed by y = RMSNorm(h; g, eps) (rows
 // < m_padded, pad rows zero); with split K the norm runs inside the reduce.
@@ -39,10 +45,25 @@ hipError_t launch_gemm_residual_norm(const bf16* a, const bf16* w, bf16* h, cons
 hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* slot, int rows,
                                  int nq, int nkv, int d, float theta, const KvDev& kv,
                                  hipStream_t s);
-// same, with each row's position and slot taken from the batch metadata
-hipError_t launch_rope_kv_append_meta(bf16* qkv, const ChunkList& chunks, const DecDev& dec,
-                                      int nq, int nkv, int d, float theta, const KvDev& kv,
-                                      hipStream_t s);
+// Per-row RoPE table of the layer path (workspace): position, KV slot (-1:
+// none) and cos / sin of the d/2 pair angles.
+struct RopeTab {
+  int32_t* pos;
+  int32_t* slot;
+  float* cs;  // [rows][d/2]
+  float* sn;
+};
+// First RMSNorm of the layer, which also fills the rows' RoPE table.
+hipError_t launch_rmsnorm_rope_table(const bf16* x, const bf16* g, bf16* y, int rows,
+                                     int rows_padded, int hidden, float eps,
+                                     const ChunkList& chunks, const DecDev& dec, const KvDev& kv,
+                                     int d, float theta, const RopeTab& tab, hipStream_t s);
+// RoPE on q / k and KV append from the table; with `part` (split-K partials of
+// the QKV projection, `splits` planes of Mp rows) the rows are first formed
+// from them and rows [rows, Mp) of qkv are zeroed.
+hipError_t launch_rope_append_wide(bf16* qkv, const float* part, int splits, int rows, int Mp,
+                                   int nq, int nkv, int d, const KvDev& kv, const RopeTab& tab,
+                                   hipStream_t s);
 
 // ws (prefill_workspace_bytes) holds key-split partials; nullptr: no split.
 size_t prefill_workspace_bytes(const ChunkList& chunks, int nq, int nkv, int d);

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
     int rows_padded, int hidden, float eps) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * kNormRowsPerBlock + (threadIdx.x >> 6);
+  const int r = blockIdx.x * kNormRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (r >= rows_padded) return;
   bf16* yr = y + (size_t)r * hidden;
   if (r >= rows) {  // padding row: zero dummy token
@@ -135,6 +135,16 @@ hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* y, int rows, int r
 // 16-byte loads of u[i .. i+8) and u[i+d/2 .. i+d/2+8).
 // Rotated q and k go back into qkv; K and V go to the row's KV slot (V
 // dimension-major inside the page).
+//
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, float theta, float* c,
+                                             float* sn) {
+  const double two_pi = 6.283185307179586476925;
+  const double inv_freq = exp2(-2.0 * (double)i / (double)d * log2((double)theta));
+  double ang = (double)pos * inv_freq;
+  ang -= two_pi * floor(ang / two_pi);
+  sincosf((float)ang, sn, c);
+}
+
 __global__ __launch_bounds__(256) void rope_kv_append_kernel(
     bf16* __restrict__ qkv, const int32_t* __restrict__ pos_in, const int32_t* __restrict__ slot_in,
     ChunkList chunks, DecDev dec, int nq, int nkv, int d, float theta, KvDev kv) {
@@ -153,13 +163,7 @@ __global__ __launch_bounds__(256) void rope_kv_append_kernel(
   const int page = slot >= 0 ? slot / kv.page_size : -1;
   const int off = slot >= 0 ? slot % kv.page_size : 0;
   __shared__ float cs_tab[64], sn_tab[64];  // d/2 <= 64
-  if (threadIdx.x < half) {
-    const double two_pi = 6.283185307179586476925;
-    const double inv_freq = exp2(-2.0 * (double)threadIdx.x / (double)d * log2((double)theta));
-    double ang = (double)pos * inv_freq;
-    ang -= two_pi * floor(ang / two_pi);
-    sincosf((float)ang, &sn_tab[threadIdx.x], &cs_tab[threadIdx.x]);
-  }
+  if (threadIdx.x < half) rope_cos_sin(pos, threadIdx.x, d, theta, &cs_tab[threadIdx.x], &sn_tab[threadIdx.x]);
   __syncthreads();
   for (int t = threadIdx.x; t < (nq + nkv) * groups; t += blockDim.x) {
     const int h = t / groups, i0 = (t % groups) * 8;
@@ -215,13 +219,162 @@ hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* s
   return hipGetLastError();
 }
 
-hipError_t launch_rope_kv_append_meta(bf16* qkv, const ChunkList& chunks, const DecDev& dec,
-                                      int nq, int nkv, int d, float theta, const KvDev& kv,
-                                      hipStream_t s) {
-  const int rows = chunks.n_rows + dec.n;
+// ---------------------------------------------------- layer path: table + wide append
+// The first RMSNorm kernel also resolves every row's position and KV slot and
+// tabulates its RoPE cos / sin, so the append kernel that follows the QKV
+// projection is pure element-wise work spread over (row, 4 heads) groups.
+template <int CH>
+__global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_rope_table_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
+    int rows_padded, int hidden, float eps, ChunkList chunks, DecDev dec, int page_size,
+    int num_pages, int d, float theta, RopeTab tab) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kNormRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (r >= rows_padded) return;
+  bf16* yr = y + (size_t)r * hidden;
+  if (r >= rows) {  // padding row: zero dummy token
+    for (int c = lane * 8; c < hidden; c += 64 * 8) *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
+    return;
+  }
+  int pos, slot;
+  row_pos_slot(chunks, dec, page_size, num_pages, r, &pos, &slot);
+  if (lane == 0) {
+    tab.pos[r] = pos;
+    tab.slot[r] = slot;
+  }
+  const int half = d >> 1;
+  if (lane < half) rope_cos_sin(pos, lane, d, theta, tab.cs + (size_t)r * half + lane,
+                                tab.sn + (size_t)r * half + lane);
+  rmsnorm_row<CH>(x + (size_t)r * hidden, g, yr, hidden, eps, lane);
+}
+
+hipError_t launch_rmsnorm_rope_table(const bf16* x, const bf16* g, bf16* y, int rows,
+                                     int rows_padded, int hidden, float eps,
+                                     const ChunkList& chunks, const DecDev& dec, const KvDev& kv,
+                                     int d, float theta, const RopeTab& tab, hipStream_t s) {
+  if (rows_padded == 0) return hipSuccess;
+  if (d / 2 > 64) return hipErrorInvalidValue;
+  const dim3 grid((rows_padded + kNormRowsPerBlock - 1) / kNormRowsPerBlock);
+  const dim3 block(64 * kNormRowsPerBlock);
+#define HL_LAUNCH_TAB(CH_)                                                                    \
+  hipLaunchKernelGGL(rmsnorm_rope_table_kernel<CH_>, grid, block, 0, s, x, g, y, rows,        \
+                     rows_padded, hidden, eps, chunks, dec, kv.page_size, kv.num_pages, d,   \
+                     theta, tab)
+  const int ch = (hidden + 511) / 512;  // 16-byte chunks per lane
+  if (ch <= 1) HL_LAUNCH_TAB(1);
+  else if (ch <= 2) HL_LAUNCH_TAB(2);
+  else if (ch <= 4) HL_LAUNCH_TAB(4);
+  else if (ch <= 8) HL_LAUNCH_TAB(8);
+  else if (ch <= 16) HL_LAUNCH_TAB(16);
+  else if (ch <= kNormMaxChunks) HL_LAUNCH_TAB(kNormMaxChunks);
+  else return hipErrorInvalidValue;
+#undef HL_LAUNCH_TAB
+  return hipGetLastError();
+}
+
+// 8 consecutive values of a row starting at column c, as bf16: from the bf16
+// row, or summed over the split-K partials in split order and rounded exactly
+// as the separate reduce does
+__device__ __forceinline__ u32x4 row8(const bf16* row, const float* part, size_t plane, int splits,
+                                      int c) {
+  if (!part) return ld16(row + c);
+  f32x4 lo = *reinterpret_cast<const f32x4*>(part + c);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(part + c + 4);
+  for (int z = 1; z < splits; ++z) {
+    lo += *reinterpret_cast<const f32x4*>(part + z * plane + c);
+    hi += *reinterpret_cast<const f32x4*>(part + z * plane + c + 4);
+  }
+  return u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
+}
+
+constexpr int kRopeHeads = 4;  // heads per workgroup of the wide append kernel
+
+// Workgroup (row r, heads 4 y .. 4 y + 3) of the q, k, v heads.  q / k heads:
+// a thread takes 8 consecutive pairs, rotates them with the row's table and
+// writes them back (k also to the row's KV slot).  v heads: a thread takes 8
+// values and writes them to the slot (dimension-major in the page).  With
+// partials the row is formed from them and written back whole, and rows in
+// [rows, Mp) are zero rows.
+__global__ __launch_bounds__(64) void rope_append_wide_kernel(
+    bf16* __restrict__ qkv, const float* __restrict__ part, int splits, int rows, int Mp, int nq,
+    int nkv, int d, KvDev kv, RopeTab tab) {
+  const int r = blockIdx.x;
+  const int h0 = blockIdx.y * kRopeHeads;
+  const int nh = nq + 2 * nkv;
+  const int ld = nh * d;
+  const int half = d >> 1;
+  bf16* row = qkv + (size_t)r * ld;
+  const int hend = min(h0 + kRopeHeads, nh);
+  if (r >= rows) {
+    for (int c = h0 * d + threadIdx.x * 8; c < hend * d; c += 64 * 8)
+      *reinterpret_cast<u32x4*>(row + c) = u32x4{0, 0, 0, 0};
+    return;
+  }
+  const float* pr = part ? part + (size_t)r * ld : nullptr;
+  const size_t plane = (size_t)Mp * ld;
+  const int slot = tab.slot[r];
+  const int page = slot >= 0 ? slot / kv.page_size : -1;
+  const int off = slot >= 0 ? slot % kv.page_size : 0;
+  const float* cs = tab.cs + (size_t)r * half;
+  const float* sn = tab.sn + (size_t)r * half;
+  const int qk_groups = half / 8;  // 8-pair groups per q / k head
+  const int v_groups = d / 8;      // 8-value groups per v head
+  // items: (head, group) over the workgroup's heads, in head order
+  int items = 0;
+  for (int h = h0; h < hend; ++h) items += h >= nq + nkv ? v_groups : qk_groups;
+  for (int it = threadIdx.x; it < items; it += 64) {
+    int h = h0, t = it;
+    while (true) {  // at most 4 heads
+      const int per = h >= nq + nkv ? v_groups : qk_groups;
+      if (t < per) break;
+      t -= per;
+      ++h;
+    }
+    bf16* u = row + h * d;
+    if (h < nq + nkv) {
+      const int i0 = t * 8;
+      const u32x4 av = row8(row, pr, plane, splits, h * d + i0);
+      const u32x4 bv = row8(row, pr, plane, splits, h * d + i0 + half);
+      u32x4 oa, ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a0 = __uint_as_float(av[e] << 16), a1 = __uint_as_float(av[e] & 0xffff0000u);
+        const float b0 = __uint_as_float(bv[e] << 16), b1 = __uint_as_float(bv[e] & 0xffff0000u);
+        const float c0 = cs[i0 + 2 * e], c1 = cs[i0 + 2 * e + 1];
+        const float s0 = sn[i0 + 2 * e], s1 = sn[i0 + 2 * e + 1];
+        oa[e] = pack2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+        ob[e] = pack2(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
+      }
+      *reinterpret_cast<u32x4*>(u + i0) = oa;
+      *reinterpret_cast<u32x4*>(u + i0 + half) = ob;
+      if (h >= nq && page >= 0) {
+        bf16* kp = kv.k_page(page, h - nq) + (size_t)off * d;
+        *reinterpret_cast<u32x4*>(kp + i0) = oa;
+        *reinterpret_cast<u32x4*>(kp + i0 + half) = ob;
+      }
+    } else {
+      const int gv = h - nq - nkv, dd = t * 8;
+      const u32x4 vv = row8(row, pr, plane, splits, h * d + dd);
+      if (pr) *reinterpret_cast<u32x4*>(u + dd) = vv;
+      if (page < 0) continue;
+      bf16* vp = kv.v_page(page, gv) + (size_t)dd * kv.page_size + off;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vp[(2 * j) * kv.page_size] = (bf16)(vv[j] & 0xffffu);
+        vp[(2 * j + 1) * kv.page_size] = (bf16)(vv[j] >> 16);
+      }
+    }
+  }
+}
+
+hipError_t launch_rope_append_wide(bf16* qkv, const float* part, int splits, int rows, int Mp,
+                                   int nq, int nkv, int d, const KvDev& kv, const RopeTab& tab,
+                                   hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_kv_append_kernel, dim3(rows), dim3(256), 0, s, qkv, nullptr, nullptr,
-                     chunks, dec, nq, nkv, d, theta, kv);
+  const int nh = nq + 2 * nkv;
+  const dim3 grid(part ? Mp : rows, (nh + kRopeHeads - 1) / kRopeHeads);
+  hipLaunchKernelGGL(rope_append_wide_kernel, grid, dim3(64), 0, s, qkv, part, splits, rows, Mp,
+                     nq, nkv, d, kv, tab);
   return hipGetLastError();
 }
 

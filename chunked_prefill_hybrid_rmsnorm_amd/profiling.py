@@ -36,9 +36,8 @@ from typing import Dict, Iterable, List, Optional, Tuple
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
-SLOTS = ("rmsnorm1", "gemm_qkv", "gemm_qkv_reduce", "rope_kv_append", "attention",
-         "attention_merge", "gemm_o", "gemm_o_reduce_rmsnorm2", "gemm_gate_up", "gemm_down",
-         "gemm_down_reduce")
+SLOTS = ("rmsnorm1", "gemm_qkv", "rope_kv_append", "attention", "attention_merge", "gemm_o",
+         "gemm_o_reduce_rmsnorm2", "gemm_gate_up", "gemm_down", "gemm_down_reduce")
 CALIBRATION_BYTES = 256 << 20
 
 
@@ -77,17 +76,17 @@ class SlotLabeler:
         if not n.startswith("hl::"):
             return None
         idx = SLOTS.index
-        if "rmsnorm_kernel" in n:
+        if "rmsnorm_rope_table" in n:
+            s = "rmsnorm1"
+        elif "rmsnorm_kernel" in n:
             # the second RMSNorm runs as a plain kernel when the O projection
             # was not split
             s = "gemm_o_reduce_rmsnorm2" if self.last == idx("gemm_o") else "rmsnorm1"
         elif "gemm_splitk_reduce_norm" in n:
             s = "gemm_o_reduce_rmsnorm2"
-        elif "gemm_splitk_reduce<0>" in n:
-            s = "gemm_qkv_reduce"
         elif "gemm_splitk_reduce<1>" in n:
             s = "gemm_down_reduce"
-        elif "rope_kv_append" in n:
+        elif "rope_append_wide" in n or "rope_kv_append" in n:
             s = "rope_kv_append"
         elif "attention_merge" in n:
             s = "attention_merge"

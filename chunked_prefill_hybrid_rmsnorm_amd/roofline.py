@@ -90,7 +90,7 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     st: List[Stage] = []
     st.append(Stage("rmsnorm1", 3 * M * H, 2 * M * H * 2 + H * 2))
     st.append(Stage("gemm_qkv", 2 * Mp * H * nqkv, H * nqkv * 2 + M * H * 2 + M * nqkv * 2))
-    st.append(Stage("gemm_qkv_reduce", 0.0, 0.0))
+    # RoPE + KV append (it also sums the QKV split-K partials: not algorithmic)
     st.append(Stage("rope_kv_append", 6 * M * (nq + nkv) * d,
                     M * nqkv * 2 + M * (nq + nkv) * d * 2 + M * kvB))
     pf_flops = 0.0

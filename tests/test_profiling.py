@@ -3,10 +3,9 @@ from chunked_prefill_hybrid_rmsnorm_amd.profiling import SLOTS, SlotLabeler
 
 GEMM = "void hl::gemm_dma_kernel<288, 128, 2, 4, {e}, 3, 64>(unsigned short const*, int)"
 SPLIT_CALL = [
-    "void hl::rmsnorm_kernel<8>(unsigned short const*)",
+    "void hl::rmsnorm_rope_table_kernel<8>(unsigned short const*)",
     GEMM.format(e=0),
-    "void hl::gemm_splitk_reduce<0>(float const*, int)",
-    "hl::rope_kv_append_kernel(unsigned short*, int const*)",
+    "hl::rope_append_wide_kernel(unsigned short*, float const*)",
     "void hl::attention_kernel<128>(hl::AttnArgs)",
     "void hl::attention_merge_kernel<128>(hl::AttnArgs)",
     GEMM.format(e=1),
@@ -16,7 +15,8 @@ SPLIT_CALL = [
     "void hl::gemm_splitk_reduce<1>(float const*, int)",
 ]
 # no split anywhere: no reduces, no merge, the second RMSNorm is a plain kernel
-PLAIN_CALL = [SPLIT_CALL[i] for i in (0, 1, 3, 4, 6, 0, 8, 9)]
+PLAIN_CALL = [SPLIT_CALL[i] for i in (0, 1, 2, 3, 5)] + [
+    "void hl::rmsnorm_kernel<8>(unsigned short const*)"] + [SPLIT_CALL[i] for i in (7, 8)]
 
 
 def test_split_call_fills_every_slot_in_order():
