@@ -125,19 +125,42 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_norm(
 // two per SIMD, behind a 3-stage copy ring), keeping >= 8 k-steps per split.
 struct Choice {
   int big;     // 1: 288-row tile, 0: 128-row tile
+  int bn96;    // 1: 96-column tile (288-row tiles of plain / residual GEMMs)
   int splits;  // K splits (1 = none)
 };
+
+// Split K (powers of two, at most 8, at least 8 k-steps per split) while the
+// workgroup count stays within one per CU.
+static int splits_for(int tiles, int ksteps) {
+  int sp = 1;
+  while (tiles * sp * 2 <= 256 && ksteps / (sp * 2) >= 8 && sp < 8) sp *= 2;
+  return sp;
+}
 
 static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   Choice c;
   c.big = mp > 128 ? 1 : 0;
+  c.bn96 = 0;
   const int bm = c.big ? 288 : 128;
-  const int out_n = epi == EPI_SWIGLU ? 64 : 128;
-  const int tiles = ((mp + bm - 1) / bm) * ((n + out_n - 1) / out_n);
+  const int mt = (mp + bm - 1) / bm;
   const int ksteps = k / kGemmBK;
-  c.splits = 1;
-  if (epi != EPI_SWIGLU)
-    while (tiles * c.splits * 2 <= 256 && ksteps / (c.splits * 2) >= 8 && c.splits < 8) c.splits *= 2;
+  if (epi == EPI_SWIGLU) {
+    c.splits = 1;
+    return c;
+  }
+  const int t128 = mt * ((n + 127) / 128);
+  c.splits = splits_for(t128, ksteps);
+  if (c.big && ksteps >= 32) {
+    // narrower tiles when they fill more CUs (QKV-like widths); they sum K in
+    // two k-groups, so short-K shapes keep the 128-column tile and with it the
+    // same per-element summation order as the 128-row tile
+    const int t96 = mt * ((n + 95) / 96);
+    const int s96 = splits_for(t96, ksteps);
+    if (t96 * s96 <= 256 && t96 * s96 > t128 * c.splits) {
+      c.bn96 = 1;
+      c.splits = s96;
+    }
+  }
   return c;
 }
 
@@ -152,6 +175,10 @@ template <int EPI>
 static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2,
                              bf16* c, const bf16* r, float* part, int m, int mp, int n, int k,
                              hipStream_t s) {
+  if constexpr (EPI != EPI_SWIGLU) {
+    if (ch.big && ch.bn96)
+      return run_gemm_dma<288, 96, 2, 2, EPI, 3, 64, 2>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  }
   if (ch.big) {
     // long k loops amortise the k-group reduction: 4 waves per group, each
     // with a 144 x 64 sub-tile (fewer LDS bytes per MFMA)

@@ -27,13 +27,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // sub-tile, so fewer LDS bytes are read per MFMA, while the workgroup still
 // holds two waves per SIMD.  The groups' partial tiles are summed through LDS
 // at the end, each group finishing half of the row fragments.
-// PIPE (one wave per SIMD, KG = 1, BK = 64): the fragments of the two
-// 32-wide halves of a stage go to two register sets, so that one half's LDS
-// reads run under the other half's MFMAs; the barrier sits between the two
-// halves, after the stage has been read completely, and the copy of the
-// next stage into the freed slot is issued there.
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1,
-          bool PIPE = false>
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1>
 __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W2,
     bf16* __restrict__ C, const bf16* __restrict__ R, float* __restrict__ part, int M, int Mp,
@@ -59,7 +53,6 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   static_assert(STAGES >= 3, "need at least three stages");
   static_assert(PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
   static_assert(KG == 1 || KG == BK / 32, "a k-group takes one 32-wide slice of a stage");
-  static_assert(!PIPE || (KG == 1 && BK == 64 && NBLK % NW == 0), "pipelined loop shape");
   static_assert(KG == 1 || NWG * FM * FN * 1024 <= STAGES * STAGE_BYTES, "reduction fits the ring");
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -149,44 +142,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   }
   // fragment rows start at multiples of 16, so the swizzle depends on l16 only
 
-  if (PIPE && nk > 0) {
-    bf16x8 aw0[FN], ax0[FM], aw1[FN], ax1[FM];
-    auto frags = [&](bf16x8 (&w)[FN], bf16x8 (&x)[FM], const char* st, int ks) {
-      const int so = swz<BK>(l16, ks * 4 + q) << 4;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) w[fn] = as_bf16x8(ld16(st + w_off[fn] + so));
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) x[fm] = as_bf16x8(ld16(st + a_off[fm] + so));
-    };
-    auto mma = [&](const bf16x8 (&w)[FN], const bf16x8 (&x)[FM]) {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma16x16x32(w[fn], x[fm], acc[fn][fm]);
-    };
-    // every slot starts filled; stage s + STAGES goes into slot s once read
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue(s);
-    wait_vmcnt<PER_WAVE * (STAGES - 1)>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    frags(aw0, ax0, smem, 0);
-    for (int it = 0; it < nk; ++it) {
-      const char* st = smem + (it % STAGES) * STAGE_BYTES;
-      frags(aw1, ax1, st, 1);
-      mma(aw0, ax0);
-      // slot it is fully read (in registers) and step it + 1 has landed
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      wait_vmcnt<PER_WAVE * (STAGES - 2)>();
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      issue(it + STAGES);
-      frags(aw0, ax0, smem + ((it + 1) % STAGES) * STAGE_BYTES, 0);
-      mma(aw1, ax1);
-    }
-  } else if (nk > 0) {
+  if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(s);
     for (int it = 0; it < nk; ++it) {
@@ -289,8 +245,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1,
-          bool PIPE = false>
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1>
 hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, const bf16* r,
                         float* part, int m, int mp, int n, int k, int splits, hipStream_t s) {
   constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
@@ -298,7 +253,7 @@ hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, c
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int mt = (mp + BM - 1) / BM, nt = (n + OUT_N - 1) / OUT_N;
   if (EPI == EPI_SWIGLU) splits = 1;
-  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK, KG, PIPE>;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK, KG>;
   // raise the dynamic LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
