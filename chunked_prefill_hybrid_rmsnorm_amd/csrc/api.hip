@@ -49,7 +49,9 @@ Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad
   L.xn2 = o;  o = align256(o + Mp * H * 2);
   L.act = o;  o = align256(o + Mp * F * 2);
   L.dec = o;
-  o = align256(o + (n_dec > 0 ? decode_workspace_bytes(n_dec, c->n_q_heads, d, max_ctx) : 0));
+  o = align256(o + (n_dec > 0
+                        ? decode_workspace_bytes(n_dec, c->n_q_heads, c->n_kv_heads, d, max_ctx)
+                        : 0));
   L.pre = o;
   o = align256(o + prefill_workspace_bound(rows, c->n_q_heads, c->n_kv_heads, (int)d));
   L.gemm = o;
@@ -127,7 +129,8 @@ int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t m
   if (e) return e;
   if (!bytes) return HL_ERR_NULL;
   if (n_decodes < 0 || max_ctx < 0) return HL_ERR_SHAPE;
-  *bytes = decode_workspace_bytes(n_decodes, cfg->n_q_heads, cfg->head_dim, max_ctx);
+  *bytes = decode_workspace_bytes(n_decodes, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim,
+                                  max_ctx);
   return HL_OK;
 }
 
@@ -431,7 +434,8 @@ int hl_decode_attention(const hl_config* cfg, const hl_bf16* qkv, int32_t row0,
   if (row0 < 0) return HL_ERR_SHAPE;
   if (dd.n == 0) return HL_OK;
   if (!ws) return HL_ERR_NULL;
-  if (ws_bytes < decode_workspace_bytes(dd.n, cfg->n_q_heads, cfg->head_dim, dd.max_ctx))
+  if (ws_bytes <
+      decode_workspace_bytes(dd.n, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, dd.max_ctx))
     return HL_ERR_WORKSPACE;
   return launch_decode_attention(reinterpret_cast<const bf16*>(qkv), row0, cfg->n_q_heads,
                                  cfg->n_kv_heads, cfg->head_dim, dd, make_kv(cfg, kv),

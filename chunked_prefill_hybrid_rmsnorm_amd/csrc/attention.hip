@@ -15,10 +15,14 @@
 // waves of a workgroup cover 64 consecutive rows and walk the same keys.  With
 // few row groups the key range is split into segments (more workgroups).
 //
-// Decode: one wave per (decode j, kv head g, 256-key partition); the G query
-// heads of kv head g are the tile rows.  Every K and V byte of the context is
-// read once.  A decode whose context fits one partition writes its output
-// directly.
+// Decode: the G query heads of kv head g are the tile rows, and every K and V
+// byte of a context is read once.  The 32-key steps of all decodes, laid end
+// to end in decode order, are cut into P equal slices per kv head, one wave
+// each, so every decode wave carries the same number of bytes whatever the
+// mix of context lengths (fixed per-decode partitions leave most waves of
+// short contexts idle and load some compute units twice as much as others).
+// A decode that falls inside one slice is finished by its wave; otherwise
+// each slice leaves a partial result for the merge.
 #include <string.h>
 
 #include "attn_common.h"
@@ -29,6 +33,8 @@ constexpr int kAttnWaves = 4;
 constexpr int kPfRowsPerWave = 32;                       // two 16-row MFMA blocks
 constexpr int kPrefillRows = kPfRowsPerWave * kAttnWaves;  // rows per prefill workgroup
 constexpr int kPfStages = 3;                             // LDS ring depth of prefill K/V
+constexpr int kDecMinSliceSteps = 4;   // fewest 32-key steps in a decode slice
+constexpr int kDecMaxWaves = 4096;     // decode waves of one launch, all kv heads
 
 struct AttnArgs {
   const bf16* qkv;
@@ -46,8 +52,9 @@ struct AttnArgs {
   // decode
   DecDev dec;
   int dc_row0;   // first decode row
-  int dc_parts;  // partitions of the longest context
-  int dc_wgs;    // decode workgroups = ceil(n * parts * nkv / 4)
+  int dc_slices;  // slices per kv head the grid provides (upper bound of P)
+  int dc_pn;      // partial slots per q head = dc_slices + n
+  int dc_wgs;     // decode workgroups = ceil(dc_slices * nkv / 4)
   float* dc_o;
   float* dc_ml;
 };
@@ -221,25 +228,45 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   }
 }
 
-static_assert(kDecodePart % 32 == 0 && kDecodePart <= 64 * 16,
-              "a decode unit is whole steps and fits one block-table window");
+// Split of the decode steps.  Slice s of P covers concatenated steps
+// [floor(s S / P), floor((s + 1) S / P)); with P <= S no slice is empty.
+struct DecodeSplit {
+  int S;  // 32-key steps of all decodes
+  int P;  // slices in use
+};
+__device__ __forceinline__ int decode_steps(int ctx) { return (ctx + 32) >> 5; }  // ceil((ctx+1)/32)
+__device__ __forceinline__ int slice_begin(int s, const DecodeSplit& d) {
+  return (int)((long long)s * d.S / d.P);
+}
+// the slice holding step t: the last s with slice_begin(s) <= t
+__device__ __forceinline__ int slice_of(int t, const DecodeSplit& d) {
+  return (int)(((long long)(t + 1) * d.P - 1) / d.S);
+}
+// S from the context lengths, and P = min(max_slices, S / kDecMinSliceSteps);
+// the attention waves and the merge compute it alike (one wave each)
+__device__ __forceinline__ DecodeSplit decode_split(const DecDev& dec, int max_slices, int lane) {
+  int S = 0;
+  for (int c0 = 0; c0 < dec.n; c0 += 64) {
+    const int j = c0 + lane;
+    const int st = j < dec.n ? decode_steps(dec.ctx_lens[j]) : 0;
+    S += __builtin_amdgcn_readlane(wave_incl_scan(st, lane), 63);
+  }
+  DecodeSplit d;
+  d.S = S;
+  d.P = max(1, min(max_slices, S / kDecMinSliceSteps));
+  return d;
+}
 
+// Steps [t0, t1) of decode j (first step cj, nj steps) for kv head g; the
+// result goes to the output row when slice s holds the whole decode, else to
+// partial slot s + j (consecutive pieces of a kv head raise s, j or both, so
+// the slot is distinct for every piece).
 template <int D>
-__device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int l16, int q) {
-  // unit = ((j * parts + part) * nkv + g): a workgroup's waves share (j, part)
-  const int g = unit % A.nkv;
-  const int jp = unit / A.nkv;
-  const int part = jp % A.dc_parts, j = jp / A.dc_parts;
-  if (j >= A.dec.n) return;
+__device__ __forceinline__ void decode_piece(const AttnArgs& A, const DecodeSplit& sp, int s,
+                                             int j, int g, int ctx, int cj, int nj, int t0, int t1,
+                                             int l16, int q) {
   const int G = A.nq / A.nkv;
-  const int ctx = A.dec.ctx_lens[j];
-  const int n_keys = ctx + 1;
-  const int k0 = part * kDecodePart;
-  if (k0 >= n_keys) return;
-  const int k1 = min(n_keys, k0 + kDecodePart);
-  const int n_parts = (n_keys + kDecodePart - 1) / kDecodePart;
   const int row = A.dc_row0 + j;
-
   const int ld = (A.nq + 2 * A.nkv) * D;
   const bf16* qrow = A.qkv + (size_t)row * ld + (size_t)(g * G) * D;
   bf16x8 qf[D / 32];
@@ -249,18 +276,52 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int l16
                      : as_bf16x8(u32x4{0, 0, 0, 0});
   AttnAcc<D> a;
   init_acc<D>(a);
-  attend_segment<D>(a, qf, ctx, k0, k1, n_keys,
-                    A.dec.block_tables + (size_t)j * A.dec.max_blocks, A.dec.max_blocks, A.kv, g,
-                    l16, q);
+  const int k0 = (t0 - cj) * 32, k1 = min((t1 - cj) * 32, ctx + 1);
+  const int32_t* bt = A.dec.block_tables + (size_t)j * A.dec.max_blocks;
+  // one block-table window (64 blocks) per call
+  for (int kk = k0; kk < k1; kk += 64 * 16)
+    attend_segment<D>(a, qf, ctx, kk, min(k1, kk + 64 * 16), ctx + 1, bt, A.dec.max_blocks, A.kv,
+                      g, l16, q);
   const float l_tot = row_total(a.l);
-  if (l16 >= G) return;
-  const int h = g * G + l16;
-  if (n_parts == 1) {
-    store_row<D>(a, l_tot, A.attn + (size_t)row * A.nq * D + (size_t)h * D, q);
-    return;
+  if (l16 < G) {
+    const int h = g * G + l16;
+    if (slice_of(cj, sp) == slice_of(cj + nj - 1, sp)) {
+      store_row<D>(a, l_tot, A.attn + (size_t)row * A.nq * D + (size_t)h * D, q);
+    } else {
+      const size_t pidx = (size_t)h * A.dc_pn + s + j;
+      store_partial<D>(a, l_tot, A.dc_o + pidx * D, A.dc_ml + pidx * 2, q);
+    }
   }
-  const size_t pidx = ((size_t)j * A.nq + h) * A.dc_parts + part;
-  store_partial<D>(a, l_tot, A.dc_o + pidx * D, A.dc_ml + pidx * 2, q);
+}
+
+// unit = s * nkv + g: the waves of a workgroup share slice s (same pages)
+template <int D>
+__device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int lane, int l16,
+                                            int q) {
+  const int g = unit % A.nkv;
+  const int s = unit / A.nkv;
+  if (s >= A.dc_slices) return;
+  const DecodeSplit sp = decode_split(A.dec, A.dc_slices, lane);
+  if (s >= sp.P) return;
+  const int b0 = slice_begin(s, sp), b1 = slice_begin(s + 1, sp);
+  int base = 0;  // steps of the decodes before this group of 64
+  for (int c0 = 0; c0 < A.dec.n && base < b1; c0 += 64) {
+    const int j = c0 + lane;
+    const int ctx = j < A.dec.n ? A.dec.ctx_lens[j] : 0;
+    const int st = j < A.dec.n ? decode_steps(ctx) : 0;
+    const int incl = base + wave_incl_scan(st, lane);
+    const int excl = incl - st;
+    uint64_t m = __ballot(st > 0 && incl > b0 && excl < b1);  // decodes overlapping the slice
+    while (m) {
+      const int i = __builtin_ctzll(m);
+      m &= m - 1;
+      const int cj = __builtin_amdgcn_readlane(excl, i);
+      const int nj = __builtin_amdgcn_readlane(st, i);
+      decode_piece<D>(A, sp, s, c0 + i, g, __builtin_amdgcn_readlane(ctx, i), cj, nj,
+                      max(cj, b0), min(cj + nj, b1), l16, q);
+    }
+    base = __builtin_amdgcn_readlane(incl, 63);
+  }
 }
 
 template <int D>
@@ -275,7 +336,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) 
   if (b < A.pf_wgs)
     prefill_block<D>(A, b, wave, lane, ring);
   else
-    decode_wave<D>(A, (b - A.pf_wgs) * kAttnWaves + wave, l16, q);
+    decode_wave<D>(A, (b - A.pf_wgs) * kAttnWaves + wave, lane, l16, q);
 }
 
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the parts a unit
@@ -321,10 +382,19 @@ __global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs A) {
   } else {
     const int j = r - A.chunks.n_rows;
     if (j >= A.dec.n) return;
-    const int n_parts = min(A.dc_parts, (A.dec.ctx_lens[j] + kDecodePart) / kDecodePart);
-    if (n_parts <= 1) return;
+    const int lane = threadIdx.x;
+    const DecodeSplit sp = decode_split(A.dec, A.dc_slices, lane);
+    int cj = 0;  // steps of the decodes before j
+    for (int c0 = 0; c0 < j; c0 += 64) {
+      const int i = c0 + lane;
+      const int st = i < j ? decode_steps(A.dec.ctx_lens[i]) : 0;
+      cj += __builtin_amdgcn_readlane(wave_incl_scan(st, lane), 63);
+    }
+    const int s_lo = slice_of(cj, sp);
+    const int s_hi = slice_of(cj + decode_steps(A.dec.ctx_lens[j]) - 1, sp);
+    if (s_lo == s_hi) return;
     orow += (size_t)(A.dc_row0 + j) * A.nq * D + (size_t)h * D;
-    merge_unit<D>(A.dc_o, A.dc_ml, ((size_t)j * A.nq + h) * A.dc_parts, n_parts, orow);
+    merge_unit<D>(A.dc_o, A.dc_ml, (size_t)h * A.dc_pn + s_lo + j, s_hi - s_lo + 1, orow);
   }
 }
 
@@ -370,11 +440,36 @@ size_t prefill_workspace_bytes(const ChunkList& chunks, int nq, int nkv, int d) 
   return (size_t)ns * chunks.n_rows * nq * (d + 2) * sizeof(float) + 256;
 }
 
-static int parts_for(int max_ctx) { return (max_ctx + 1 + kDecodePart - 1) / kDecodePart; }
+// Most decode slices per kv head a launch can use: bounded by the wave budget
+// and by the steps n decodes of at most max_ctx + 1 keys can have.
+static int decode_slice_cap(int n, int nkv, int max_ctx) {
+  const long long steps = (long long)n * ((max_ctx + 32) / 32);
+  return (int)max(1LL, min((long long)(kDecMaxWaves / nkv), steps / kDecMinSliceSteps));
+}
 
-size_t decode_workspace_bytes(int n_decodes, int nq, int d, int max_ctx) {
-  const size_t parts = (size_t)parts_for(max_ctx);
-  return (size_t)n_decodes * nq * parts * (d + 2) * sizeof(float) + 256;
+size_t decode_workspace_bytes(int n_decodes, int nq, int nkv, int d, int max_ctx) {
+  const size_t pn = (size_t)decode_slice_cap(n_decodes, nkv, max_ctx) + n_decodes;
+  return (size_t)nq * pn * (d + 2) * sizeof(float) + 256;
+}
+
+// Workgroups of attention_kernel<D> the device holds at once (cached per device).
+static int attention_slots(int d) {
+  static int cache[2][64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int& c = cache[d == 128 ? 1 : 0][dev];
+  if (c == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    hipError_t e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                  &per_cu, attention_kernel<128>, 64 * kAttnWaves, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                  &per_cu, attention_kernel<64>, 64 * kAttnWaves, 0);
+    if (e != hipSuccess || per_cu <= 0) per_cu = 1;
+    c = max(1, cus * per_cu);
+  }
+  return c;
 }
 
 hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const ChunkList& chunks,
@@ -409,15 +504,21 @@ hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const Chunk
   A.dec = dec;
   A.dc_row0 = dec_row0;
   if (dec.n > 0) {
-    A.dc_parts = parts_for(dec.max_ctx);
-    A.dc_wgs = (dec.n * A.dc_parts * nkv + kAttnWaves - 1) / kAttnWaves;
+    // decode waves fill the workgroup slots the prefill part leaves free, so
+    // that both kinds run side by side (at least a quarter of the slots)
+    const int slots = attention_slots(d);
+    const int free_wgs = max(slots - A.pf_wgs, slots / 4);
+    A.dc_slices =
+        max(1, min(free_wgs * kAttnWaves / nkv, decode_slice_cap(dec.n, nkv, dec.max_ctx)));
+    A.dc_pn = A.dc_slices + dec.n;
+    A.dc_wgs = (A.dc_slices * nkv + kAttnWaves - 1) / kAttnWaves;
     A.dc_o = reinterpret_cast<float*>(dc_ws);
-    A.dc_ml = A.dc_o + (size_t)dec.n * nq * A.dc_parts * d;
+    A.dc_ml = A.dc_o + (size_t)nq * A.dc_pn * d;
   }
   const int wgs = A.pf_wgs + A.dc_wgs;
   if (wgs == 0) return mid ? hipEventRecord(mid, s) : hipSuccess;
   const int merge_rows = chunks.n_rows + dec.n;
-  const bool merge = A.pf_ns > 1 || A.dc_parts > 1;
+  const bool merge = A.pf_ns > 1 || A.dc_slices > 1;
   if (d == 128)
     hipLaunchKernelGGL(attention_kernel<128>, dim3(wgs), dim3(64 * kAttnWaves), 0, s, A);
   else

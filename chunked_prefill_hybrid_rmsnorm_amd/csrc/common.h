@@ -16,11 +16,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-// Tokens per decode-attention partition (split-K unit).
-#ifndef HL_DECODE_PART
-#define HL_DECODE_PART 256
-#endif
-constexpr int kDecodePart = HL_DECODE_PART;  // keys per decode work unit
 
 __device__ __forceinline__ float bf2f(bf16 b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -56,6 +51,15 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// inclusive prefix sum over the wave's lanes
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
   return v;
 }
 

@@ -72,7 +72,7 @@ hipError_t launch_prefill_attention(const bf16* qkv, int nq, int nkv, int d,
                                     const ChunkList& chunks, const KvDev& kv, bf16* attn,
                                     void* ws, hipStream_t s);
 
-size_t decode_workspace_bytes(int n_decodes, int nq, int d, int max_ctx);
+size_t decode_workspace_bytes(int n_decodes, int nq, int nkv, int d, int max_ctx);
 // Prefill rows and decode rows in one launch (plus one merge when keys were
 // split); pf_ws / dc_ws as for the two launchers below.
 hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const ChunkList& chunks,
