@@ -214,9 +214,10 @@ struct PageWindow {
 
 // Keys [k0, k1) of one decode (k0 a multiple of 32, at most 64 blocks, so one
 // block-table window covers them) through its block table.  Every step loads
-// its fragments one step ahead, and every half of the loop issues exactly one
-// step's loads (the last one repeats the final step), so the wait before a
-// multiply covers only the loads of that step.
+// its fragments one step ahead.  The loop body always issues exactly two
+// steps' loads and the last one or two steps are peeled off, so the count of
+// loads in flight is the same on every path: the wait before a multiply
+// covers only the loads of that step, and no load goes past the last step.
 template <int D>
 __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)[D / 32],
                                                int row_limit, int k0, int k1, int kv_len,
@@ -229,8 +230,8 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
   PageWindow win;
   win.fill(bt, n_blocks, blk0, blk_end, kv.num_pages, lane);
   const int nst = (k1 - k0 + 31) / 32;
-  auto load = [&](KvFrag<D>& f, int st) {  // step st, clamped to the last one
-    const int b = blk0 + 2 * min(st, nst - 1);
+  auto load = [&](KvFrag<D>& f, int st) {
+    const int b = blk0 + 2 * st;
     const int p0 = b < blk_end ? __builtin_amdgcn_readlane(win.page, b - blk0) : -1;
     const int p1 = b + 1 < blk_end ? __builtin_amdgcn_readlane(win.page, b + 1 - blk0) : -1;
     load_step<D>(f, kv, g, p0, p1, l16, q);
@@ -243,14 +244,21 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
   const int lm[1] = {wave_min(row_limit)};
   // keys from block blk_end on come from a stand-in page: zero their V
   const int v_end = min(kv_len, blk_end * 16);
-  // an odd step count gets one more step past k1: all its keys are masked
   KvFrag<D> fa, fb;
   load(fa, 0);
-  for (int i = 0; i < nst; i += 2) {
+  int i = 0;
+  for (; i + 2 < nst; i += 2) {
     load(fb, i + 1);
     compute_step<D, 1>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
     load(fa, i + 2);
     compute_step<D, 1>(ab, fb, qb, k0 + 32 * (i + 1), rl, lm, k1, v_end, scale, q);
+  }
+  if (i + 1 < nst) {  // two steps left, the first already loaded
+    load(fb, i + 1);
+    compute_step<D, 1>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
+    compute_step<D, 1>(ab, fb, qb, k0 + 32 * (i + 1), rl, lm, k1, v_end, scale, q);
+  } else {
+    compute_step<D, 1>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
   }
   a = ab[0];
 }
