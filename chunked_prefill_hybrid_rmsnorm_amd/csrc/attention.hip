@@ -182,8 +182,8 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   const int nsteps = (k1 - k0 + 31) / 32;
   // keys from block blk_end on are read from a stand-in page: zero their V
   const int v_end = min(kv_len, blk_end * 16);
-  // copies of step s (clamped to the last step; pages past the table read page
-  // 0, whose keys are masked) so every wave issues the same count each step
+  // copies of step s (pages past the table read page 0, whose keys are
+  // masked); every wave issues the same copies, and none past the last step
   auto issue = [&](int s) {
     const int t = k0 + min(s, nsteps - 1) * 32;
     int p0 = win.at(t, ch.block_table, ch.n_blocks, blk_end, A.kv.num_pages, lane);
@@ -196,21 +196,25 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   init_acc<D>(a[0]);
   init_acc<D>(a[1]);
   const float scale = kAttnLog2e * rsqrtf((float)D);
-#pragma unroll
-  for (int s = 0; s < kPfStages - 1; ++s) issue(s);
+  static_assert(kPfStages == 3, "the waits below count one step in flight behind the current");
+  issue(0);
+  if (nsteps > 1) issue(1);
   for (int i = 0; i < nsteps; ++i) {
-    wait_vmcnt<PfStage<D>::PER_WAVE * (kPfStages - 2)>();
+    // this step's copies have landed (the next step's may still be in flight)
+    if (i + 1 < nsteps)
+      wait_vmcnt<PfStage<D>::PER_WAVE>();
+    else
+      wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(i + kPfStages - 1);
+    if (i + 2 < nsteps) issue(i + 2);
     if (!busy) continue;
     KvFrag<D> f;
     prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
     const int t0 = k0 + i * 32;
     compute_step<D, 2>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale, q);
   }
-  wait_vmcnt<0>();  // the clamped tail copies land before the workgroup ends
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const float l_tot = row_total(a[rb].l);
@@ -339,8 +343,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) 
     decode_wave<D>(A, (b - A.pf_wgs) * kAttnWaves + wave, lane, l16, q);
 }
 
-// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the parts a unit
-// (row, head) used; a unit with one part was written directly.
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the parts of one
+// (row, head), stored consecutively from `base`; lane i takes dims D/64 i ...
 template <int D>
 __device__ __forceinline__ void merge_unit(const float* __restrict__ o_part,
                                            const float* __restrict__ ml_part, size_t base,
@@ -365,7 +369,10 @@ __device__ __forceinline__ void merge_unit(const float* __restrict__ o_part,
   for (int i = 0; i < PER; ++i) orow[threadIdx.x * PER + i] = f2bf(o[i] * inv);
 }
 
-// one 64-thread block per (row, q head); grid.y spans chunk rows then decodes
+// One 64-thread block per (row, q head), rows being the chunk rows and then
+// the decodes: many small independent blocks, so that their load latencies
+// overlap.  Rows whose keys were not split were written by the attention
+// kernel.
 template <int D>
 __global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs A) {
   const int h = blockIdx.x, r = blockIdx.y;
@@ -399,9 +406,16 @@ __global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs A) {
 }
 
 // ---------------------------------------------------------------- host side
-// Prefill key split: only when the chunk rows give fewer than 256 workgroups,
-// into segments of >= 256 keys (multiples of 32), aiming at ~512 workgroups.
-void prefill_split(const ChunkList& chunks, int nq, int nkv, int* nsplit, int* seg) {
+// Prefill key split: only when the chunk rows give few workgroups, into
+// segments of >= 256 keys (multiples of 32).  Prefill alone aims at ~512
+// workgroups (split below 256).  Beside decodes it aims at 128 (split below
+// 128): there the decode waves set the kernel time, every prefill workgroup
+// takes a slot a decode wave group could use, and every split adds partials
+// for the merge to read.
+constexpr int kPfAimAlone = 512, kPfAimHybrid = 128;
+
+void prefill_split(const ChunkList& chunks, int nq, int nkv, bool with_decodes, int* nsplit,
+                   int* seg) {
   const int G = nq / nkv;
   int base = 0, max_keys = 0;
   for (int i = 0; i < chunks.n; ++i) {
@@ -409,7 +423,9 @@ void prefill_split(const ChunkList& chunks, int nq, int nkv, int* nsplit, int* s
     max_keys = max(max_keys, chunks.c[i].start_pos + chunks.c[i].len);
   }
   int ns = 1;
-  if (base > 0 && base < 256) ns = min((512 + base - 1) / base, max(1, max_keys / 256));
+  const int aim = with_decodes ? kPfAimHybrid : kPfAimAlone;
+  const int below = with_decodes ? kPfAimHybrid : kPfAimAlone / 2;
+  if (base > 0 && base < below) ns = min((aim + base - 1) / base, max(1, max_keys / 256));
   ns = max(ns, 1);
   int sg = (max_keys + ns - 1) / ns;
   sg = (sg + 31) / 32 * 32;
@@ -418,16 +434,17 @@ void prefill_split(const ChunkList& chunks, int nq, int nkv, int* nsplit, int* s
   *nsplit = max(1, (max_keys + sg - 1) / sg);
 }
 
-// Upper bound of prefill_workspace_bytes over every chunk layout with at most
-// `rows` chunk rows (any start positions): the split count is at most
-// ceil(512 / base) with base >= ceil(r G / 64) nkv workgroups for r rows.
+// Upper bound of the prefill partials over every chunk layout with at most
+// `rows` chunk rows (any start positions), with or without decodes: the split
+// count is at most ceil(kPfAimAlone / base) with base >= ceil(r G /
+// kPrefillRows) nkv workgroups for r rows.
 size_t prefill_workspace_bound(int rows, int nq, int nkv, int d) {
   const int G = nq / nkv;
   size_t worst = 0;
   for (int r = 1; r <= rows; ++r) {
     const int base = (r * G + kPrefillRows - 1) / kPrefillRows * nkv;
-    if (base >= 256) continue;
-    const size_t ns = (512 + base - 1) / base;
+    if (base >= kPfAimAlone / 2) continue;
+    const size_t ns = (kPfAimAlone + base - 1) / base;
     worst = max(worst, ns * (size_t)r);
   }
   return worst ? worst * nq * (d + 2) * sizeof(float) + 256 : 0;
@@ -435,7 +452,7 @@ size_t prefill_workspace_bound(int rows, int nq, int nkv, int d) {
 
 size_t prefill_workspace_bytes(const ChunkList& chunks, int nq, int nkv, int d) {
   int ns, sg;
-  prefill_split(chunks, nq, nkv, &ns, &sg);
+  prefill_split(chunks, nq, nkv, false, &ns, &sg);
   if (ns <= 1) return 0;
   return (size_t)ns * chunks.n_rows * nq * (d + 2) * sizeof(float) + 256;
 }
@@ -491,7 +508,7 @@ hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const Chunk
     A.pf_ns = 1;
     A.pf_seg = 1 << 30;
     if (pf_ws) {
-      prefill_split(chunks, nq, nkv, &A.pf_ns, &A.pf_seg);
+      prefill_split(chunks, nq, nkv, dec.n > 0, &A.pf_ns, &A.pf_seg);
       if (A.pf_ns <= 1) {
         A.pf_ns = 1;
         A.pf_seg = 1 << 30;
