@@ -345,24 +345,45 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) 
 
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the parts of one
 // (row, head), stored consecutively from `base`; lane i takes dims D/64 i ...
+// Parts are loaded 8 at a time (indices clamped to the last part), so their
+// load latencies overlap; they are summed in part order.
 template <int D>
 __device__ __forceinline__ void merge_unit(const float* __restrict__ o_part,
                                            const float* __restrict__ ml_part, size_t base,
                                            int n_parts, bf16* __restrict__ orow) {
+  constexpr int U = 8;
   float mmax = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) mmax = fmaxf(mmax, ml_part[(base + p) * 2]);
+  for (int p0 = 0; p0 < n_parts; p0 += U) {
+    float mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mv[u] = ml_part[(base + min(p0 + u, n_parts - 1)) * 2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mmax = fmaxf(mmax, mv[u]);
+  }
   constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
   float lsum = 0.f;
-  for (int p = 0; p < n_parts; ++p) {
-    const float mp = ml_part[(base + p) * 2];
-    if (mp == -INFINITY) continue;  // no visible key in this part
-    const float w = exp2f(mp - mmax);
-    lsum += w * ml_part[(base + p) * 2 + 1];
+  for (int p0 = 0; p0 < n_parts; p0 += U) {
+    float mv[U], lv[U], ov[U][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] += w * o_part[(base + p) * D + threadIdx.x * PER + i];
+    for (int u = 0; u < U; ++u) {
+      const size_t pi = base + min(p0 + u, n_parts - 1);
+      mv[u] = ml_part[pi * 2];
+      lv[u] = ml_part[pi * 2 + 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ov[u][i] = o_part[pi * D + threadIdx.x * PER + i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // past the last part, or no visible key in this part
+      if (p0 + u >= n_parts || mv[u] == -INFINITY) continue;
+      const float w = exp2f(mv[u] - mmax);
+      lsum += w * lv[u];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += w * ov[u][i];
+    }
   }
   const float inv = 1.f / lsum;
 #pragma unroll

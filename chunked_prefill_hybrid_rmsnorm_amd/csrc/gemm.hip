@@ -26,8 +26,11 @@
 namespace hl {
 
 // ------------------------------------------------------------ split-K reduce
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_splitk_reduce(const float* __restrict__ part, int splits,
+// The split count is a template parameter: every split's loads are issued
+// before the first is waited for (a loop over a runtime count waits for each
+// split in turn).  Splits are summed in split order.
+template <int EPI, int SPLITS>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce(const float* __restrict__ part,
                                                           bf16* __restrict__ C,
                                                           const bf16* __restrict__ R, int M, int Mp,
                                                           int N) {
@@ -37,8 +40,13 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(const float* __restric
   if (idx >= mlim * n4) return;
   const int m = idx / n4, n = (idx % n4) * 4;
   const size_t plane = (size_t)Mp * N;
-  f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)m * N + n);
-  for (int z = 1; z < splits; ++z) v += *reinterpret_cast<const f32x4*>(part + z * plane + (size_t)m * N + n);
+  f32x4 pv[SPLITS];
+#pragma unroll
+  for (int z = 0; z < SPLITS; ++z)
+    pv[z] = *reinterpret_cast<const f32x4*>(part + z * plane + (size_t)m * N + n);
+  f32x4 v = pv[0];
+#pragma unroll
+  for (int z = 1; z < SPLITS; ++z) v += pv[z];
   if (EPI == EPI_RESIDUAL) {
     const u32x2 rr = ld8(R + (size_t)m * N + n);
     v[0] += __uint_as_float(rr[0] << 16);
@@ -57,9 +65,9 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(const float* __restric
 // per pass), adds the residual, stores h (bf16) and y = h / sqrt(mean(h^2) +
 // eps) * g computed from that stored h.  Rows in [M, Mp) get y = 0 (dummy
 // tokens).  N = hidden, a multiple of 64, at most 256 * 8 * CH.
-template <int CH>
+template <int CH, int SPLITS>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_norm(
-    const float* __restrict__ part, int splits, bf16* __restrict__ H_out,
+    const float* __restrict__ part, bf16* __restrict__ H_out,
     const bf16* __restrict__ R, const bf16* __restrict__ g, bf16* __restrict__ Y, int M, int Mp,
     int N, float eps) {
   const int tid = threadIdx.x;
@@ -70,22 +78,31 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_norm(
     return;
   }
   const size_t plane = (size_t)Mp * N;
-  u32x4 hv[CH];
+  u32x4 hv[CH], gvr[CH];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = (i * 256 + tid) * 8;
     if (c >= N) {
       hv[i] = u32x4{0, 0, 0, 0};
+      gvr[i] = u32x4{0, 0, 0, 0};
       continue;
     }
     const float* p = part + (size_t)m * N + c;
-    f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-    for (int z = 1; z < splits; ++z) {
-      a += *reinterpret_cast<const f32x4*>(p + z * plane);
-      b += *reinterpret_cast<const f32x4*>(p + z * plane + 4);
+    f32x4 pa[SPLITS], pb[SPLITS];
+#pragma unroll
+    for (int z = 0; z < SPLITS; ++z) {
+      pa[z] = *reinterpret_cast<const f32x4*>(p + z * plane);
+      pb[z] = *reinterpret_cast<const f32x4*>(p + z * plane + 4);
     }
     const u32x4 rr = ld16(R + (size_t)m * N + c);
+    gvr[i] = ld16(g + c);  // the gains go out with the partials, not after the row sum
+    f32x4 a = pa[0], b = pb[0];
+#pragma unroll
+    for (int z = 1; z < SPLITS; ++z) {
+      a += pa[z];
+      b += pb[z];
+    }
     const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -105,7 +122,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_norm(
   for (int i = 0; i < CH; ++i) {
     const int c = (i * 256 + tid) * 8;
     if (c >= N) continue;
-    const u32x4 gv = ld16(g + c);
+    const u32x4 gv = gvr[i];
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -130,7 +147,8 @@ struct Choice {
 };
 
 // Split K (powers of two, at most 8, at least 8 k-steps per split) while the
-// workgroup count stays within one per CU.
+// workgroup count stays within one per CU.  The reduce kernels are
+// instantiated for 2, 4 and 8 splits.
 static int splits_for(int tiles, int ksteps) {
   int sp = 1;
   while (tiles * sp * 2 <= 256 && ksteps / (sp * 2) >= 8 && sp < 8) sp *= 2;
@@ -223,20 +241,34 @@ hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf1
   const int mlim = epi == EPI_RESIDUAL ? m : m_padded;
   const int threads = mlim * (n / 4);
   if (threads == 0) return hipSuccess;
-  if (epi == EPI_RESIDUAL)
-    hipLaunchKernelGGL(gemm_splitk_reduce<EPI_RESIDUAL>, dim3((threads + 255) / 256), dim3(256), 0,
-                       s, part, ch.splits, c, residual, m, m_padded, n);
-  else
-    hipLaunchKernelGGL(gemm_splitk_reduce<EPI_STORE>, dim3((threads + 255) / 256), dim3(256), 0,
-                       s, part, ch.splits, c, residual, m, m_padded, n);
+  const dim3 grid((threads + 255) / 256), block(256);
+#define HL_REDUCE(E_, S_) \
+  hipLaunchKernelGGL((gemm_splitk_reduce<E_, S_>), grid, block, 0, s, part, c, residual, m, m_padded, n)
+  if (epi == EPI_RESIDUAL) {
+    if (ch.splits == 2) HL_REDUCE(EPI_RESIDUAL, 2);
+    else if (ch.splits == 4) HL_REDUCE(EPI_RESIDUAL, 4);
+    else HL_REDUCE(EPI_RESIDUAL, 8);
+  } else {
+    if (ch.splits == 2) HL_REDUCE(EPI_STORE, 2);
+    else if (ch.splits == 4) HL_REDUCE(EPI_STORE, 4);
+    else HL_REDUCE(EPI_STORE, 8);
+  }
+#undef HL_REDUCE
   return hipGetLastError();
 }
 
 template <int CH>
 static void launch_rn(const float* part, int splits, bf16* h, const bf16* r, const bf16* g,
                       bf16* y, int m, int mp, int n, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_splitk_reduce_norm<CH>, dim3(mp), dim3(256), 0, s, part, splits, h, r, g,
-                     y, m, mp, n, eps);
+  if (splits == 2)
+    hipLaunchKernelGGL((gemm_splitk_reduce_norm<CH, 2>), dim3(mp), dim3(256), 0, s, part, h, r, g,
+                       y, m, mp, n, eps);
+  else if (splits == 4)
+    hipLaunchKernelGGL((gemm_splitk_reduce_norm<CH, 4>), dim3(mp), dim3(256), 0, s, part, h, r, g,
+                       y, m, mp, n, eps);
+  else
+    hipLaunchKernelGGL((gemm_splitk_reduce_norm<CH, 8>), dim3(mp), dim3(256), 0, s, part, h, r, g,
+                       y, m, mp, n, eps);
 }
 
 hipError_t launch_gemm_residual_norm(const bf16* a, const bf16* w, bf16* h, const bf16* residual,

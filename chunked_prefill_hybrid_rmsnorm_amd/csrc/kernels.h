@@ -47,6 +47,13 @@ hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* s
                                  hipStream_t s);
 // Per-row RoPE table of the layer path (workspace): position, KV slot (-1:
 // none) and cos / sin of the d/2 pair angles.
+// theta^(-2 i / d) for the rotation pairs of a head (d / 2 <= kRopeMaxPairs),
+// computed on the host in fp64 and passed by value
+constexpr int kRopeMaxPairs = 64;
+struct RopeFreq {
+  double inv[kRopeMaxPairs];
+};
+
 struct RopeTab {
   int32_t* pos;
   int32_t* slot;

@@ -2,6 +2,8 @@
 // the hybrid-batch layer.
 #include <string.h>
 
+#include <cmath>
+
 #include "kernels.h"
 
 namespace hl {
@@ -57,37 +59,60 @@ hipError_t launch_slot_map(const ChunkList& chunks, const DecDev& dec, int page_
 constexpr int kNormRowsPerBlock = 4;
 constexpr int kNormMaxChunks = 32;  // 16-byte chunks per lane: hidden <= 16384
 
+// One row per wave, in two halves so that a caller can put other work
+// between issuing the loads and using them: the row and the gain vector are
+// loaded together (one memory round trip), then reduced, scaled and stored.
 template <int CH>
-__device__ __forceinline__ void rmsnorm_row(const bf16* __restrict__ xr, const bf16* __restrict__ g,
-                                            bf16* __restrict__ yr, int hidden, float eps, int lane) {
-  u32x4 v[CH];
-  float ss = 0.f;
+struct NormRow {
+  u32x4 v[CH], g[CH];
+};
+
+template <int CH>
+__device__ __forceinline__ void rmsnorm_load(NormRow<CH>& n, const bf16* __restrict__ xr,
+                                             const bf16* __restrict__ g, int hidden, int lane) {
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = (i * 64 + lane) * 8;
-    v[i] = c < hidden ? ld16(xr + c) : u32x4{0, 0, 0, 0};
+    n.v[i] = c < hidden ? ld16(xr + c) : u32x4{0, 0, 0, 0};
+    n.g[i] = c < hidden ? ld16(g + c) : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void rmsnorm_finish(const NormRow<CH>& n, bf16* __restrict__ yr,
+                                               int hidden, float eps, int lane) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = __uint_as_float(v[i][e] << 16), b = __uint_as_float(v[i][e] & 0xffff0000u);
+      const float a = __uint_as_float(n.v[i][e] << 16), b = __uint_as_float(n.v[i][e] & 0xffff0000u);
       ss += a * a + b * b;
     }
-  }
   ss = wave_sum(ss);
   const float inv = rsqrtf(ss / (float)hidden + eps);
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = (i * 64 + lane) * 8;
     if (c >= hidden) continue;
-    const u32x4 gv = ld16(g + c);
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = __uint_as_float(v[i][e] << 16) * inv * __uint_as_float(gv[e] << 16);
-      const float b = __uint_as_float(v[i][e] & 0xffff0000u) * inv * __uint_as_float(gv[e] & 0xffff0000u);
+      const float a = __uint_as_float(n.v[i][e] << 16) * inv * __uint_as_float(n.g[i][e] << 16);
+      const float b = __uint_as_float(n.v[i][e] & 0xffff0000u) * inv *
+                      __uint_as_float(n.g[i][e] & 0xffff0000u);
       o[e] = pack2(a, b);
     }
     *reinterpret_cast<u32x4*>(yr + c) = o;
   }
+}
+
+template <int CH>
+__device__ __forceinline__ void rmsnorm_row(const bf16* __restrict__ xr, const bf16* __restrict__ g,
+                                            bf16* __restrict__ yr, int hidden, float eps, int lane) {
+  NormRow<CH> n;
+  rmsnorm_load<CH>(n, xr, g, hidden, lane);
+  rmsnorm_finish<CH>(n, yr, hidden, eps, lane);
 }
 
 template <int CH>
@@ -136,18 +161,26 @@ hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* y, int rows, int r
 // Rotated q and k go back into qkv; K and V go to the row's KV slot (V
 // dimension-major inside the page).
 //
-__device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, float theta, float* c,
-                                             float* sn) {
-  const double two_pi = 6.283185307179586476925;
-  const double inv_freq = exp2(-2.0 * (double)i / (double)d * log2((double)theta));
+// cos / sin of pos * inv_freq: the angle is formed and reduced to [0, 2 pi)
+// in fp64, the functions are taken in fp32
+__device__ __forceinline__ void rope_cos_sin(int pos, double inv_freq, float* c, float* sn) {
+  const double two_pi = 6.283185307179586476925, inv_two_pi = 0.15915494309189533576888;
   double ang = (double)pos * inv_freq;
-  ang -= two_pi * floor(ang / two_pi);
+  ang -= two_pi * floor(ang * inv_two_pi);
   sincosf((float)ang, sn, c);
+}
+
+// theta^(-2 i / d) for the d / 2 rotation pairs, in fp64 (host side)
+static RopeFreq rope_freq(int d, float theta) {
+  RopeFreq f;
+  for (int i = 0; i < kRopeMaxPairs; ++i)
+    f.inv[i] = i < d / 2 ? std::exp2(-2.0 * i / d * std::log2((double)theta)) : 0.0;
+  return f;
 }
 
 __global__ __launch_bounds__(256) void rope_kv_append_kernel(
     bf16* __restrict__ qkv, const int32_t* __restrict__ pos_in, const int32_t* __restrict__ slot_in,
-    ChunkList chunks, DecDev dec, int nq, int nkv, int d, float theta, KvDev kv) {
+    ChunkList chunks, DecDev dec, int nq, int nkv, int d, RopeFreq freq, KvDev kv) {
   const int r = blockIdx.x;
   const int half = d >> 1;
   const int groups = half / 8;  // 8-pair groups per head
@@ -163,7 +196,8 @@ __global__ __launch_bounds__(256) void rope_kv_append_kernel(
   const int page = slot >= 0 ? slot / kv.page_size : -1;
   const int off = slot >= 0 ? slot % kv.page_size : 0;
   __shared__ float cs_tab[64], sn_tab[64];  // d/2 <= 64
-  if (threadIdx.x < half) rope_cos_sin(pos, threadIdx.x, d, theta, &cs_tab[threadIdx.x], &sn_tab[threadIdx.x]);
+  if (threadIdx.x < half)
+    rope_cos_sin(pos, freq.inv[threadIdx.x], &cs_tab[threadIdx.x], &sn_tab[threadIdx.x]);
   __syncthreads();
   for (int t = threadIdx.x; t < (nq + nkv) * groups; t += blockDim.x) {
     const int h = t / groups, i0 = (t % groups) * 8;
@@ -214,8 +248,9 @@ hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* s
   ChunkList none_c;
   memset(&none_c, 0, sizeof(none_c));
   DecDev none_d{};
+  if (d / 2 > kRopeMaxPairs) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rope_kv_append_kernel, dim3(rows), dim3(256), 0, s, qkv, pos, slot, none_c,
-                     none_d, nq, nkv, d, theta, kv);
+                     none_d, nq, nkv, d, rope_freq(d, theta), kv);
   return hipGetLastError();
 }
 
@@ -227,7 +262,7 @@ template <int CH>
 __global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_rope_table_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
     int rows_padded, int hidden, float eps, ChunkList chunks, DecDev dec, int page_size,
-    int num_pages, int d, float theta, RopeTab tab) {
+    int num_pages, int d, RopeFreq freq, RopeTab tab) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * kNormRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (r >= rows_padded) return;
@@ -236,6 +271,9 @@ __global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_rope_table_ker
     for (int c = lane * 8; c < hidden; c += 64 * 8) *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
     return;
   }
+  // the row's loads go out first; the table is worked out while they are in flight
+  NormRow<CH> n;
+  rmsnorm_load<CH>(n, x + (size_t)r * hidden, g, hidden, lane);
   int pos, slot;
   row_pos_slot(chunks, dec, page_size, num_pages, r, &pos, &slot);
   if (lane == 0) {
@@ -243,9 +281,10 @@ __global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_rope_table_ker
     tab.slot[r] = slot;
   }
   const int half = d >> 1;
-  if (lane < half) rope_cos_sin(pos, lane, d, theta, tab.cs + (size_t)r * half + lane,
-                                tab.sn + (size_t)r * half + lane);
-  rmsnorm_row<CH>(x + (size_t)r * hidden, g, yr, hidden, eps, lane);
+  if (lane < half)
+    rope_cos_sin(pos, freq.inv[lane], tab.cs + (size_t)r * half + lane,
+                 tab.sn + (size_t)r * half + lane);
+  rmsnorm_finish<CH>(n, yr, hidden, eps, lane);
 }
 
 hipError_t launch_rmsnorm_rope_table(const bf16* x, const bf16* g, bf16* y, int rows,
@@ -253,13 +292,14 @@ hipError_t launch_rmsnorm_rope_table(const bf16* x, const bf16* g, bf16* y, int 
                                      const ChunkList& chunks, const DecDev& dec, const KvDev& kv,
                                      int d, float theta, const RopeTab& tab, hipStream_t s) {
   if (rows_padded == 0) return hipSuccess;
-  if (d / 2 > 64) return hipErrorInvalidValue;
+  if (d / 2 > kRopeMaxPairs) return hipErrorInvalidValue;
+  const RopeFreq freq = rope_freq(d, theta);
   const dim3 grid((rows_padded + kNormRowsPerBlock - 1) / kNormRowsPerBlock);
   const dim3 block(64 * kNormRowsPerBlock);
 #define HL_LAUNCH_TAB(CH_)                                                                    \
   hipLaunchKernelGGL(rmsnorm_rope_table_kernel<CH_>, grid, block, 0, s, x, g, y, rows,        \
                      rows_padded, hidden, eps, chunks, dec, kv.page_size, kv.num_pages, d,   \
-                     theta, tab)
+                     freq, tab)
   const int ch = (hidden + 511) / 512;  // 16-byte chunks per lane
   if (ch <= 1) HL_LAUNCH_TAB(1);
   else if (ch <= 2) HL_LAUNCH_TAB(2);
@@ -273,18 +313,27 @@ hipError_t launch_rmsnorm_rope_table(const bf16* x, const bf16* g, bf16* y, int 
 }
 
 // 8 consecutive values of a row starting at column c, as bf16: from the bf16
-// row, or summed over the split-K partials in split order and rounded exactly
-// as the separate reduce does
-__device__ __forceinline__ u32x4 row8(const bf16* row, const float* part, size_t plane, int splits,
-                                      int c) {
-  if (!part) return ld16(row + c);
-  f32x4 lo = *reinterpret_cast<const f32x4*>(part + c);
-  f32x4 hi = *reinterpret_cast<const f32x4*>(part + c + 4);
-  for (int z = 1; z < splits; ++z) {
-    lo += *reinterpret_cast<const f32x4*>(part + z * plane + c);
-    hi += *reinterpret_cast<const f32x4*>(part + z * plane + c + 4);
+// row (SPLITS = 0), or summed over SPLITS split-K partials in split order and
+// rounded exactly as the separate reduce does (all loads issued first)
+template <int SPLITS>
+__device__ __forceinline__ u32x4 row8(const bf16* row, const float* part, size_t plane, int c) {
+  if constexpr (SPLITS == 0) {
+    return ld16(row + c);
+  } else {
+    f32x4 plo[SPLITS], phi[SPLITS];
+#pragma unroll
+    for (int z = 0; z < SPLITS; ++z) {
+      plo[z] = *reinterpret_cast<const f32x4*>(part + z * plane + c);
+      phi[z] = *reinterpret_cast<const f32x4*>(part + z * plane + c + 4);
+    }
+    f32x4 lo = plo[0], hi = phi[0];
+#pragma unroll
+    for (int z = 1; z < SPLITS; ++z) {
+      lo += plo[z];
+      hi += phi[z];
+    }
+    return u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
   }
-  return u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
 }
 
 constexpr int kRopeHeads = 4;  // heads per workgroup of the wide append kernel
@@ -293,11 +342,12 @@ constexpr int kRopeHeads = 4;  // heads per workgroup of the wide append kernel
 // a thread takes 8 consecutive pairs, rotates them with the row's table and
 // writes them back (k also to the row's KV slot).  v heads: a thread takes 8
 // values and writes them to the slot (dimension-major in the page).  With
-// partials the row is formed from them and written back whole, and rows in
-// [rows, Mp) are zero rows.
+// partials (SPLITS > 0 of them) the row is formed from them and written back
+// whole, and rows in [rows, Mp) are zero rows.
+template <int SPLITS>
 __global__ __launch_bounds__(64) void rope_append_wide_kernel(
-    bf16* __restrict__ qkv, const float* __restrict__ part, int splits, int rows, int Mp, int nq,
-    int nkv, int d, KvDev kv, RopeTab tab) {
+    bf16* __restrict__ qkv, const float* __restrict__ part, int rows, int Mp, int nq, int nkv,
+    int d, KvDev kv, RopeTab tab) {
   const int r = blockIdx.x;
   const int h0 = blockIdx.y * kRopeHeads;
   const int nh = nq + 2 * nkv;
@@ -333,8 +383,8 @@ __global__ __launch_bounds__(64) void rope_append_wide_kernel(
     bf16* u = row + h * d;
     if (h < nq + nkv) {
       const int i0 = t * 8;
-      const u32x4 av = row8(row, pr, plane, splits, h * d + i0);
-      const u32x4 bv = row8(row, pr, plane, splits, h * d + i0 + half);
+      const u32x4 av = row8<SPLITS>(row, pr, plane, h * d + i0);
+      const u32x4 bv = row8<SPLITS>(row, pr, plane, h * d + i0 + half);
       u32x4 oa, ob;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -354,7 +404,7 @@ __global__ __launch_bounds__(64) void rope_append_wide_kernel(
       }
     } else {
       const int gv = h - nq - nkv, dd = t * 8;
-      const u32x4 vv = row8(row, pr, plane, splits, h * d + dd);
+      const u32x4 vv = row8<SPLITS>(row, pr, plane, h * d + dd);
       if (pr) *reinterpret_cast<u32x4*>(u + dd) = vv;
       if (page < 0) continue;
       bf16* vp = kv.v_page(page, gv) + (size_t)dd * kv.page_size + off;
@@ -373,8 +423,15 @@ hipError_t launch_rope_append_wide(bf16* qkv, const float* part, int splits, int
   if (rows == 0) return hipSuccess;
   const int nh = nq + 2 * nkv;
   const dim3 grid(part ? Mp : rows, (nh + kRopeHeads - 1) / kRopeHeads);
-  hipLaunchKernelGGL(rope_append_wide_kernel, grid, dim3(64), 0, s, qkv, part, splits, rows, Mp,
-                     nq, nkv, d, kv, tab);
+#define HL_ROPE(S_)                                                                          \
+  hipLaunchKernelGGL(rope_append_wide_kernel<S_>, grid, dim3(64), 0, s, qkv, part, rows, Mp, nq, \
+                     nkv, d, kv, tab)
+  if (!part) HL_ROPE(0);
+  else if (splits == 2) HL_ROPE(2);
+  else if (splits == 4) HL_ROPE(4);
+  else if (splits == 8) HL_ROPE(8);
+  else return hipErrorInvalidValue;
+#undef HL_ROPE
   return hipGetLastError();
 }
 
