@@ -39,8 +39,10 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    # ~25 ms of layer calls before the timed region: with 10 the GPU's clocks
+    # are still ramping and a step reads ~6 % slower than in steady state
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", choices=["mistral", "llama70", "tiny"], default="mistral")
     p.add_argument("--pad", type=int, default=16)
     p.add_argument("--rotate", type=int, default=4)
