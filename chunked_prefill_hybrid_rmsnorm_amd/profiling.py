@@ -84,7 +84,7 @@ class SlotLabeler:
             s = "gemm_o_reduce_rmsnorm2" if self.last == idx("gemm_o") else "rmsnorm1"
         elif "gemm_splitk_reduce_norm" in n:
             s = "gemm_o_reduce_rmsnorm2"
-        elif "gemm_splitk_reduce<1>" in n:
+        elif re.search(r"gemm_splitk_reduce<1[,>]", n):  # <EPI_RESIDUAL[, splits]>
             s = "gemm_down_reduce"
         elif "rope_append_wide" in n or "rope_kv_append" in n:
             s = "rope_kv_append"
@@ -117,15 +117,16 @@ def _rows(path: str) -> List[dict]:
     return rows
 
 
-def kernel_durations(trace_csv: str) -> Dict[str, List[float]]:
-    """Per slot, the duration (ns) of every dispatch in a kernel trace."""
+def kernel_durations(trace_csv: str, skip: int = 0) -> Dict[str, List[float]]:
+    """Per slot, the duration (ns) of every dispatch in a kernel trace, without
+    the first `skip` dispatches of each slot (the GPU's clock ramp)."""
     lab = SlotLabeler()
     out: Dict[str, List[float]] = defaultdict(list)
     for r in _rows(trace_csv):
         s = lab.label(r["Kernel_Name"])
         if s:
             out[s].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
-    return out
+    return {k: v[skip:] if len(v) > skip else v for k, v in out.items()}
 
 
 def counter_values(counter_csv: str, counter: str) -> Tuple[Dict[str, List[float]], float]:
@@ -152,9 +153,10 @@ def _mean(v: Iterable[float]) -> float:
     return sum(v) / len(v) if v else 0.0
 
 
-def summarize(trace_csv: Optional[str], fetch_csv: Optional[str], write_csv: Optional[str]):
+def summarize(trace_csv: Optional[str], fetch_csv: Optional[str], write_csv: Optional[str],
+              skip: int = 0):
     res = {"slots": {}}
-    durs = kernel_durations(trace_csv) if trace_csv else {}
+    durs = kernel_durations(trace_csv, skip) if trace_csv else {}
     fetch, fcal = counter_values(fetch_csv, "FETCH_SIZE") if fetch_csv else ({}, 0.0)
     write, wcal = counter_values(write_csv, "WRITE_SIZE") if write_csv else ({}, 0.0)
     fscale = CALIBRATION_BYTES / (fcal * 1024) if fcal else None
@@ -237,8 +239,10 @@ def main():
     p.add_argument("--command", action="append", default=[])
     p.add_argument("--md")
     p.add_argument("--traffic")
+    p.add_argument("--skip", type=int, default=0,
+                   help="drop the first N dispatches of each slot (clock ramp)")
     a = p.parse_args()
-    res = summarize(a.trace, a.fetch, a.write)
+    res = summarize(a.trace, a.fetch, a.write, a.skip)
     if a.md:
         write_markdown(a.md, res, a.workload, a.command)
     if a.traffic:

@@ -5,14 +5,14 @@ GEMM = "void hl::gemm_dma_kernel<288, 128, 2, 4, {e}, 3, 64>(unsigned short cons
 SPLIT_CALL = [
     "void hl::rmsnorm_rope_table_kernel<8>(unsigned short const*)",
     GEMM.format(e=0),
-    "hl::rope_append_wide_kernel(unsigned short*, float const*)",
+    "void hl::rope_append_wide_kernel<4>(unsigned short*, float const*)",
     "void hl::attention_kernel<128>(hl::AttnArgs)",
     "void hl::attention_merge_kernel<128>(hl::AttnArgs)",
     GEMM.format(e=1),
-    "void hl::gemm_splitk_reduce_norm<2>(float const*, int)",
+    "void hl::gemm_splitk_reduce_norm<2, 8>(float const*, unsigned short*)",
     GEMM.format(e=2),
     GEMM.format(e=1),
-    "void hl::gemm_splitk_reduce<1>(float const*, int)",
+    "void hl::gemm_splitk_reduce<1, 8>(float const*, unsigned short*)",
 ]
 # no split anywhere: no reduces, no merge, the second RMSNorm is a plain kernel
 PLAIN_CALL = [SPLIT_CALL[i] for i in (0, 1, 2, 3, 5)] + [
@@ -29,6 +29,12 @@ def test_unsplit_call_labels():
     got = [lab.label(k) for k in PLAIN_CALL + SPLIT_CALL[:2]]
     assert got == ["rmsnorm1", "gemm_qkv", "rope_kv_append", "attention", "gemm_o",
                    "gemm_o_reduce_rmsnorm2", "gemm_gate_up", "gemm_down", "rmsnorm1", "gemm_qkv"]
+
+
+def test_reduce_of_a_plain_gemm_is_not_the_down_reduce():
+    lab = SlotLabeler()
+    lab.label(GEMM.format(e=0))
+    assert lab.label("void hl::gemm_splitk_reduce<0, 4>(float const*, unsigned short*)") is None
 
 
 def test_foreign_kernels_are_skipped():
