@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--workload", choices=["mistral", "llama70", "tiny"], default="mistral")
     p.add_argument("--pad", type=int, default=16)
     p.add_argument("--rotate", type=int, default=4)
+    p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-runs", type=int, default=2)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -156,6 +157,24 @@ def main():
     tok_s = M / (ms / 1e3)
     log(f"layer {ms * 1e3:.1f} us/step, {tok_s / 1e6:.3f} M tokens/s")
 
+    # the same calls recorded once per rotation copy into HIP graphs and
+    # replayed: removes the host-side launch cost of the layer's kernels
+    graph = None
+    if not a.no_graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        for i in range(len(copies)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                layer(i)
+            graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gms = time_loop(lambda i: graphs[i % len(graphs)].replay(), a.steps, a.warmup)
+        graph = {"ms_per_step": round(gms, 5), "value": round(M / (gms / 1e3), 1)}
+        log(f"layer (graph replay) {gms * 1e3:.1f} us/step, {M / (gms / 1e3) / 1e6:.3f} M tokens/s")
+
     # per-step times inside the real layer sequence: HIP events recorded by the
     # library between its steps, on the stream it launches on
     log("per-step timing with stage events ...")
@@ -228,6 +247,7 @@ def main():
         "layer_roofline": {"t_roof_us": round(t_roof * 1e6, 2), "t_us": round(ms * 1e3, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
         "stages": table,
+        "graph_replay": graph,
     }
     if not a.no_cpu_baseline:
         log("timing the CPU oracle ...")
