@@ -43,7 +43,8 @@ def parse():
     # ~25 ms of layer calls before the timed region: with 10 the GPU's clocks
     # are still ramping and a step reads ~6 % slower than in steady state
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", choices=["mistral", "llama70", "tiny"], default="mistral")
+    p.add_argument("--workload", choices=["mistral", "llama70", "tiny", "llama70_tp8", "mistral_tp4"],
+                   default="mistral")
     p.add_argument("--pad", type=int, default=16)
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
@@ -62,6 +63,14 @@ def make_batch(name):
     if name == "llama70":
         return I.llama70_batch(seed=0), (
             "llama2-70b-shaped layer: Lp=512 (3584 cached) + Bd=64 decodes, ctx U[512,4096]")
+    if name == "llama70_tp8":
+        return I.llama70_tp8_batch(seed=0), (
+            "llama2-70b layer, one GPU's tensor-parallel share (T=8: 8 q / 1 kv heads, F=3584): "
+            "Lp=512 (3584 cached) + Bd=64 decodes, ctx U[512,4096]")
+    if name == "mistral_tp4":
+        return I.mistral_tp4_batch(seed=0), (
+            "mistral7b layer, one GPU's tensor-parallel share (T=4: 8 q / 2 kv heads, F=3584): "
+            "Lp=256 (768 cached) + Bd=32 decodes, ctx U[128,2048]")
     return I.tiny_batch(seed=0), "tiny layer H=256: Lp=64 (64 cached) + Bd=4 decodes, ctx U[16,128]"
 
 

@@ -222,7 +222,7 @@ def hl_layer_forward(cfg, weights: hl_weights, x, chunks: Sequence[hl_chunk], de
     _check(rc, "hl_layer_forward")
 
 
-N_STAGES = 10
+N_STAGES = 11
 
 
 def stage_names():

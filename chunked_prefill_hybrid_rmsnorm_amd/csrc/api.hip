@@ -58,7 +58,8 @@ Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad
   const int nqd = c->n_q_heads * c->head_dim;
   const size_t g = std::max({gemm_workspace_bytes(EPI_STORE, L.Mp, (int)nqkv, (int)H),
                              gemm_workspace_bytes(EPI_RESIDUAL, L.Mp, (int)H, nqd),
-                             gemm_workspace_bytes(EPI_RESIDUAL, L.Mp, (int)H, (int)F)});
+                             gemm_workspace_bytes(EPI_RESIDUAL, L.Mp, (int)H, (int)F),
+                             gemm_workspace_bytes(EPI_SWIGLU, L.Mp, (int)F, (int)H)});
   o = align256(o + g);
   L.total = o;
   return L;
@@ -135,9 +136,9 @@ int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t m
 }
 
 static const char* const kStageNames[HL_N_STAGES] = {
-    "rmsnorm1",  "gemm_qkv",       "rope_kv_append",         "attention",
-    "attention_merge", "gemm_o",  "gemm_o_reduce_rmsnorm2", "gemm_gate_up",
-    "gemm_down", "gemm_down_reduce"};
+    "rmsnorm1",     "gemm_qkv",  "rope_kv_append",   "attention",
+    "attention_merge", "gemm_o", "gemm_o_reduce_rmsnorm2", "gemm_gate_up",
+    "gemm_gate_up_reduce", "gemm_down", "gemm_down_reduce"};
 
 const char* hl_stage_name(int stage) {
   return (stage >= 0 && stage < HL_N_STAGES) ? kStageNames[stage] : "";
@@ -240,8 +241,8 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
   HL_MARK();
   // gate/up projection + SwiGLU
   HL_TRY(launch_gemm(EPI_SWIGLU, xn2, reinterpret_cast<const bf16*>(w->w_gate),
-                     reinterpret_cast<const bf16*>(w->w_up), act, nullptr, nullptr, M, Mp, F, H,
-                     stream));
+                     reinterpret_cast<const bf16*>(w->w_up), act, nullptr, gws, M, Mp, F, H,
+                     stream, mid()));
   HL_MARK();
   // down projection + residual
   HL_TRY(launch_gemm(EPI_RESIDUAL, act, reinterpret_cast<const bf16*>(w->w_down), nullptr,

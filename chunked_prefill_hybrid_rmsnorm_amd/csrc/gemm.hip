@@ -60,6 +60,37 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(const float* __restric
   *reinterpret_cast<u32x2*>(C + (size_t)m * N + n) = o;
 }
 
+// Split-K reduce of the gate/up GEMM: act = silu(sum gate) * (sum up) over
+// the [SPLITS][Mp][2N] partials (gate in columns [0, N), up in [N, 2N)), all
+// Mp rows (pad rows come out 0 as in the unsplit epilogue).
+template <int SPLITS>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_swiglu(const float* __restrict__ part,
+                                                                 bf16* __restrict__ act, int Mp,
+                                                                 int N) {
+  const int n4 = N / 4;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= Mp * n4) return;
+  const int m = idx / n4, n = (idx % n4) * 4;
+  const size_t plane = (size_t)Mp * 2 * N;
+  const float* p = part + (size_t)m * 2 * N + n;
+  f32x4 gv[SPLITS], uv[SPLITS];
+#pragma unroll
+  for (int z = 0; z < SPLITS; ++z) {
+    gv[z] = *reinterpret_cast<const f32x4*>(p + z * plane);
+    uv[z] = *reinterpret_cast<const f32x4*>(p + z * plane + N);
+  }
+  f32x4 g = gv[0], u = uv[0];
+#pragma unroll
+  for (int z = 1; z < SPLITS; ++z) {
+    g += gv[z];
+    u += uv[z];
+  }
+  u32x2 o;
+  o[0] = pack2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
+  o[1] = pack2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
+  *reinterpret_cast<u32x2*>(act + (size_t)m * N + n) = o;
+}
+
 // Split-K reduce of a residual GEMM fused with the RMSNorm that follows it:
 // one 256-thread workgroup per row sums the partials (8 columns per thread
 // per pass), adds the residual, stores h (bf16) and y = h / sqrt(mean(h^2) +
@@ -163,7 +194,9 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   const int mt = (mp + bm - 1) / bm;
   const int ksteps = k / kGemmBK;
   if (epi == EPI_SWIGLU) {
-    c.splits = 1;
+    // a tile yields 64 outputs (gate and up rows side by side); narrow FFN
+    // shares (tensor-parallel shapes) need K splits to fill the CUs
+    c.splits = splits_for(mt * ((n + 63) / 64), ksteps);
     return c;
   }
   const int t128 = mt * ((n + 127) / 128);
@@ -186,7 +219,8 @@ int gemm_splits(GemmEpilogue epi, int mp, int n, int k) { return choose(epi, mp,
 
 size_t gemm_workspace_bytes(GemmEpilogue epi, int mp, int n, int k) {
   const Choice c = choose(epi, mp, n, k);
-  return c.splits > 1 ? (size_t)c.splits * mp * n * sizeof(float) : 0;
+  const size_t width = epi == EPI_SWIGLU ? 2 * (size_t)n : (size_t)n;  // gate and up partials
+  return c.splits > 1 ? (size_t)c.splits * mp * width * sizeof(float) : 0;
 }
 
 template <int EPI>
@@ -238,6 +272,17 @@ hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf1
   if (e != hipSuccess) return e;
   if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   if (ch.splits == 1) return hipSuccess;
+  if (epi == EPI_SWIGLU) {
+    const int threads = m_padded * (n / 4);
+    const dim3 grid((threads + 255) / 256), block(256);
+    if (ch.splits == 2)
+      hipLaunchKernelGGL(gemm_splitk_reduce_swiglu<2>, grid, block, 0, s, part, c, m_padded, n);
+    else if (ch.splits == 4)
+      hipLaunchKernelGGL(gemm_splitk_reduce_swiglu<4>, grid, block, 0, s, part, c, m_padded, n);
+    else
+      hipLaunchKernelGGL(gemm_splitk_reduce_swiglu<8>, grid, block, 0, s, part, c, m_padded, n);
+    return hipGetLastError();
+  }
   const int mlim = epi == EPI_RESIDUAL ? m : m_padded;
   const int threads = mlim * (n / 4);
   if (threads == 0) return hipSuccess;

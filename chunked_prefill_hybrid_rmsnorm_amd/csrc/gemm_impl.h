@@ -199,6 +199,18 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   for (int fm = 0; fm < FM; ++fm) {
     if (KG > 1 && (fm < FSPLIT) != (kg == 0)) continue;
     const int m = m0 + wm * WTM + fm * 16 + l16;
+    if (splits > 1 && EPI == EPI_SWIGLU) {
+      // split-K SwiGLU: gate and up partial sums side by side, [splits][Mp][2N]
+      if (m >= Mp) continue;
+      float* pp = part + ((size_t)z * Mp + m) * 2 * N;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const bool up = fn >= FN / 2;
+        const int n = n0 + wn * (WTN / 2) + (up ? fn - FN / 2 : fn) * 16 + 4 * q;
+        if (n < N) *reinterpret_cast<f32x4*>(pp + (up ? N : 0) + n) = acc[fn][fm];
+      }
+      continue;
+    }
     if (splits > 1) {
       if (m >= Mp) continue;
       float* pp = part + (size_t)z * Mp * N + (size_t)m * N;
@@ -252,7 +264,6 @@ hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, c
   constexpr size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int mt = (mp + BM - 1) / BM, nt = (n + OUT_N - 1) / OUT_N;
-  if (EPI == EPI_SWIGLU) splits = 1;
   auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK, KG>;
   // raise the dynamic LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr = hipFuncSetAttribute(

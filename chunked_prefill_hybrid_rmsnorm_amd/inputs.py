@@ -68,6 +68,11 @@ TINY = LayerShape(256, 4, 2, 64, 1024)
 MISTRAL_7B = LayerShape(4096, 32, 8, 128, 14336)
 # Llama-2-70B-shaped layer: H=8192, 64 q / 8 kv heads, head_dim 128, FFN 28672.
 LLAMA2_70B = LayerShape(8192, 64, 8, 128, 28672)
+# One GPU's share of a tensor-parallel layer (heads and FFN columns split T
+# ways, hidden size whole): the per-GPU kernel shapes of Llama-2-70B at T = 8
+# and Mistral-7B at T = 4.
+LLAMA2_70B_TP8 = LayerShape(8192, 8, 1, 128, 3584)
+MISTRAL_7B_TP4 = LayerShape(4096, 8, 2, 128, 3584)
 
 
 # ---------------------------------------------------------------- bf16 bits
@@ -290,6 +295,22 @@ def llama70_batch(seed: int = 0, random_gains: bool = False, **kw) -> HybridBatc
                 seed=seed, weight_std=0.01, random_gains=random_gains)
     args.update(kw)
     return make_hybrid_batch(LLAMA2_70B, **args)
+
+
+def llama70_tp8_batch(seed: int = 0, random_gains: bool = False, **kw) -> HybridBatch:
+    """The Llama-2-70B batch on one GPU's tensor-parallel share (T = 8)."""
+    args = dict(chunk_lens=[512], chunk_starts=[3584], n_decodes=64, ctx_range=(512, 4096),
+                seed=seed, weight_std=0.01, random_gains=random_gains)
+    args.update(kw)
+    return make_hybrid_batch(LLAMA2_70B_TP8, **args)
+
+
+def mistral_tp4_batch(seed: int = 0, random_gains: bool = False, **kw) -> HybridBatch:
+    """The Mistral-7B batch on one GPU's tensor-parallel share (T = 4)."""
+    args = dict(chunk_lens=[256], chunk_starts=[768], n_decodes=32, ctx_range=(128, 2048),
+                seed=seed, weight_std=0.02, random_gains=random_gains)
+    args.update(kw)
+    return make_hybrid_batch(MISTRAL_7B_TP4, **args)
 
 
 def sweep_batch(lp: int, bd: int, seed: int = 0, **kw) -> HybridBatch:

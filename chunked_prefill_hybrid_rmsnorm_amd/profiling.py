@@ -37,7 +37,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 SLOTS = ("rmsnorm1", "gemm_qkv", "rope_kv_append", "attention", "attention_merge", "gemm_o",
-         "gemm_o_reduce_rmsnorm2", "gemm_gate_up", "gemm_down", "gemm_down_reduce")
+         "gemm_o_reduce_rmsnorm2", "gemm_gate_up", "gemm_gate_up_reduce", "gemm_down",
+         "gemm_down_reduce")
 CALIBRATION_BYTES = 256 << 20
 
 
@@ -82,6 +83,8 @@ class SlotLabeler:
             # the second RMSNorm runs as a plain kernel when the O projection
             # was not split
             s = "gemm_o_reduce_rmsnorm2" if self.last == idx("gemm_o") else "rmsnorm1"
+        elif "gemm_splitk_reduce_swiglu" in n:
+            s = "gemm_gate_up_reduce"
         elif "gemm_splitk_reduce_norm" in n:
             s = "gemm_o_reduce_rmsnorm2"
         elif re.search(r"gemm_splitk_reduce<1[,>]", n):  # <EPI_RESIDUAL[, splits]>

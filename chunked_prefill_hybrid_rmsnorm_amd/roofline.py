@@ -109,6 +109,7 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     # RMSNorm of h inside the reduce: xn2 out and the gain
     st.append(Stage("gemm_o_reduce_rmsnorm2", 3 * M * H, M * H * 2 + H * 2))
     st.append(Stage("gemm_gate_up", 2 * Mp * H * 2 * F, 2 * F * H * 2 + M * H * 2 + M * F * 2))
+    st.append(Stage("gemm_gate_up_reduce", 0.0, 0.0))
     st.append(Stage("gemm_down", 2 * Mp * F * H, F * H * 2 + M * F * 2 + 2 * M * H * 2))
     st.append(Stage("gemm_down_reduce", 0.0, 0.0))
     for s in st:

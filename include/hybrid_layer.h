@@ -157,7 +157,7 @@ int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x
  * not needed for this batch (a split-K reduce or a key-split merge that the
  * launch shape makes unnecessary) times as an empty interval.  hl_stage_name(i)
  * names slot i. */
-#define HL_N_STAGES 10
+#define HL_N_STAGES 11
 int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
                            const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
                            const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,

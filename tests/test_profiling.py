@@ -11,12 +11,13 @@ SPLIT_CALL = [
     GEMM.format(e=1),
     "void hl::gemm_splitk_reduce_norm<2, 8>(float const*, unsigned short*)",
     GEMM.format(e=2),
+    "void hl::gemm_splitk_reduce_swiglu<4>(float const*, unsigned short*, int, int)",
     GEMM.format(e=1),
     "void hl::gemm_splitk_reduce<1, 8>(float const*, unsigned short*)",
 ]
 # no split anywhere: no reduces, no merge, the second RMSNorm is a plain kernel
 PLAIN_CALL = [SPLIT_CALL[i] for i in (0, 1, 2, 3, 5)] + [
-    "void hl::rmsnorm_kernel<8>(unsigned short const*)"] + [SPLIT_CALL[i] for i in (7, 8)]
+    "void hl::rmsnorm_kernel<8>(unsigned short const*)"] + [SPLIT_CALL[i] for i in (7, 9)]
 
 
 def test_split_call_fills_every_slot_in_order():

@@ -42,7 +42,7 @@ def test_mistral_weight_bytes():
     decode_bytes = 32 * 1001 * MISTRAL_7B.kv_bytes_per_token + 2 * 32 * 4096 * 2
     assert by["attention"].bytes == prefill_bytes + decode_bytes
     assert by["gemm_o_reduce_rmsnorm2"].bytes == 288 * 4096 * 2 + 4096 * 2
-    for k in ("attention_merge", "gemm_down_reduce"):
+    for k in ("attention_merge", "gemm_gate_up_reduce", "gemm_down_reduce"):
         assert by[k].bytes == 0 and by[k].flops == 0
     # below the ridge (~312 flop/B) the weight-streaming GEMMs are HBM-bound
     assert by["gemm_gate_up"].bound == "hbm"
