@@ -90,6 +90,10 @@ _SIGS = {
     "hl_gemm_workspace_bytes": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _P(_c.c_size_t)]),
     "hl_gemm_swiglu": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_int32, _c.c_int32, _c.c_int32, _c.c_void_p]),
+    "hl_embed_rows": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p,
+                                 _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
+    "hl_argmax_rows": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p,
+                                  _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_void_p]),
     "hl_rope_kv_append": (_c.c_int, [_P(hl_config), _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                      _c.c_int32, _P(hl_kv), _c.c_void_p]),
     "hl_prefill_attention": (_c.c_int, [_P(hl_config), _c.c_void_p, _P(hl_chunk), _c.c_int32,
@@ -275,6 +279,19 @@ def hl_gemm_bf16(a, w, c, residual, m, m_padded, n, k, ws=None, ws_bytes=0, stre
 def hl_gemm_swiglu(a, w_gate, w_up, act, m_padded, f, k, stream=None):
     _check(load().hl_gemm_swiglu(_ptr(a), _ptr(w_gate), _ptr(w_up), _ptr(act), m_padded, f, k,
                                  _stream(stream)), "hl_gemm_swiglu")
+
+
+def hl_embed_rows(table, vocab, hidden, row_tok, last_tok, rows, out, stream=None):
+    n_last = 0 if last_tok is None else last_tok.numel()
+    _check(load().hl_embed_rows(_ptr(table), vocab, hidden, _ptr(row_tok), _ptr(last_tok), n_last,
+                                rows, _ptr(out), _stream(stream)), "hl_embed_rows")
+
+
+def hl_argmax_rows(logits, rows, vocab, sample_req, sample_pos, last_tok, out_tokens,
+                   stream=None):
+    _check(load().hl_argmax_rows(_ptr(logits), rows, vocab, _ptr(sample_req), _ptr(sample_pos),
+                                 _ptr(last_tok), last_tok.numel(), _ptr(out_tokens),
+                                 out_tokens.numel(), _stream(stream)), "hl_argmax_rows")
 
 
 def hl_rope_kv_append(cfg, qkv, positions, slots, rows, kv: hl_kv, stream=None):

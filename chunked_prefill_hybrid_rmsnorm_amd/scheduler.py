@@ -1,0 +1,127 @@
+"""Stall-free batching for a token budget (host side).
+
+Sarathi-Serve digest, Algorithm 3 (the flow of one iteration): every
+iteration forms one hybrid batch of at most ``budget`` rows --
+
+1. one decode token for every admitted request whose prompt is fully
+   prefilled (decodes are never held back by prefill);
+2. the next chunk of the request whose prompt is partly prefilled, if any:
+   ``min(prompt left, budget left)`` tokens (with new requests admitted only
+   while budget is left, at most one prompt is ever partly prefilled);
+3. new requests in arrival order while budget is left, each with a chunk of
+   ``min(prompt, budget left)`` tokens.
+
+A chunk that completes its prompt yields the request's first generated token
+from its last row; every decode row yields the next one.  A request leaves
+after ``gen_len`` generated tokens (there is no end-of-sequence token), so
+decode steps feed generated tokens 0 .. gen_len - 2.
+
+Row order inside a batch is the library's: chunk rows (in chunk order), then
+decode rows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+
+@dataclass
+class Request:
+    rid: int
+    prompt_len: int
+    gen_len: int
+    prefilled: int = 0
+    generated: int = 0
+
+    @property
+    def prefill_done(self) -> bool:
+        return self.prefilled >= self.prompt_len
+
+    @property
+    def done(self) -> bool:
+        return self.generated >= self.gen_len
+
+
+@dataclass
+class ChunkWork:
+    rid: int
+    start: int   # position of the chunk's first token
+    length: int
+
+
+@dataclass
+class Batch:
+    chunks: List[ChunkWork]
+    decodes: List[int]                 # request ids, one row each
+    # (row, request id, index of the generated token the row yields)
+    samples: List[Tuple[int, int, int]] = field(default_factory=list)
+
+    @property
+    def n_chunk_rows(self) -> int:
+        return sum(c.length for c in self.chunks)
+
+    @property
+    def n_rows(self) -> int:
+        return self.n_chunk_rows + len(self.decodes)
+
+
+class StallFreeScheduler:
+    """Requests all arrive at the start, in ``prompt_lens`` order."""
+
+    def __init__(self, prompt_lens: Sequence[int], gen_len: int, budget: int):
+        if budget <= 0 or gen_len <= 0 or any(p <= 0 for p in prompt_lens):
+            raise ValueError("budget, gen_len and every prompt length must be positive")
+        self.budget = budget
+        self.reqs = [Request(i, int(p), gen_len) for i, p in enumerate(prompt_lens)]
+        self.waiting: List[int] = list(range(len(self.reqs)))
+        self.running: List[int] = []   # admitted and not finished, in admission order
+
+    @property
+    def finished(self) -> bool:
+        return not self.waiting and not self.running
+
+    def next_batch(self) -> Optional[Batch]:
+        if self.finished:
+            return None
+        R = self.reqs
+        decodes = [r for r in self.running if R[r].prefill_done]
+        n_t = len(decodes)
+        chunks: List[ChunkWork] = []
+        partial = [r for r in self.running if not R[r].prefill_done]
+        assert len(partial) <= 1, "more than one prompt partly prefilled"
+        for r in partial:
+            c = min(R[r].prompt_len - R[r].prefilled, self.budget - n_t)
+            if c > 0:
+                chunks.append(ChunkWork(r, R[r].prefilled, c))
+                n_t += c
+        while self.waiting and n_t < self.budget:
+            r = self.waiting.pop(0)
+            self.running.append(r)
+            c = min(R[r].prompt_len, self.budget - n_t)
+            chunks.append(ChunkWork(r, 0, c))
+            n_t += c
+        b = Batch(chunks, decodes)
+        row = 0
+        for ch in chunks:
+            row += ch.length
+            if ch.start + ch.length == R[ch.rid].prompt_len:
+                b.samples.append((row - 1, ch.rid, 0))
+        for k, r in enumerate(decodes):
+            b.samples.append((b.n_chunk_rows + k, r, R[r].generated))
+        return b
+
+    def decode_context(self, rid: int) -> int:
+        """Cached tokens before a decode row of request ``rid`` (its position):
+        the prompt plus every generated token but the one it feeds."""
+        r = self.reqs[rid]
+        return r.prompt_len + r.generated - 1
+
+    def commit(self, b: Batch) -> None:
+        R = self.reqs
+        for ch in b.chunks:
+            R[ch.rid].prefilled += ch.length
+            if R[ch.rid].prefill_done:
+                R[ch.rid].generated = 1
+        for r in b.decodes:
+            R[r].generated += 1
+        self.running = [r for r in self.running if not R[r].done]

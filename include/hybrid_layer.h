@@ -222,7 +222,8 @@ int hl_prefill_attention(const hl_config* cfg, const hl_bf16* qkv, const hl_chun
 int hl_prefill_workspace_bytes(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,
                                size_t* bytes);
 
-/* Paged decode attention, split-K over 256-key partitions plus a merge.
+/* Paged decode attention.  The 32-key steps of all decodes are cut into equal
+ * slices, one per wave, and decodes split over slices are merged afterwards.
  * Decode j reads its q from qkv row row0 + j and writes attn row row0 + j.
  * ws needs hl_decode_workspace_bytes(). */
 int hl_decode_attention(const hl_config* cfg, const hl_bf16* qkv, int32_t row0,
@@ -230,6 +231,32 @@ int hl_decode_attention(const hl_config* cfg, const hl_bf16* qkv, int32_t row0,
                         size_t ws_bytes, hipStream_t stream);
 int hl_decode_workspace_bytes(const hl_config* cfg, int32_t n_decodes, int32_t max_ctx,
                               size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * Around the layers, for a batching loop (Sarathi-Serve digest, Algorithm 3:
+ * each iteration runs one hybrid batch and every decode row, and every chunk
+ * that finishes its prompt, yields one new token; greedy choice).
+ */
+
+/* out[r] = table[id_r] for r < rows, where id_r = row_tok[r] when >= 0, else
+ * last_tok[-(row_tok[r] + 1)] (the token last chosen for that request slot).
+ * table [vocab, hidden] bf16 (hidden a multiple of 8), out [rows, hidden];
+ * row_tok [rows] and last_tok [n_last] are device int32.  Ids outside
+ * [0, vocab) and slots outside [0, n_last) are clamped to the nearest valid
+ * one (no read past the arrays).  last_tok may be NULL when n_last == 0. */
+int hl_embed_rows(const hl_bf16* table, int32_t vocab, int32_t hidden, const int32_t* row_tok,
+                  const int32_t* last_tok, int32_t n_last, int32_t rows, hl_bf16* out,
+                  hipStream_t stream);
+
+/* Greedy next token of the rows that sample: for each r < rows with
+ * 0 <= sample_req[r] < n_last, the id of the largest of logits[r][0..vocab)
+ * (ties: the lowest id; NaN never wins; a row with no number gives 0) is
+ * written to last_tok[sample_req[r]] and, when 0 <= sample_pos[r] < n_out, to
+ * out_tokens[sample_pos[r]].  logits [rows, vocab] bf16; every other array is
+ * device int32.  Rows with sample_req[r] < 0 are skipped. */
+int hl_argmax_rows(const hl_bf16* logits, int32_t rows, int32_t vocab, const int32_t* sample_req,
+                   const int32_t* sample_pos, int32_t* last_tok, int32_t n_last,
+                   int32_t* out_tokens, int32_t n_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,3 +20,4 @@ from .layer import (  # noqa: F401
     slot_of,
     swiglu_ffn,
 )
+from .model import embed, greedy, model_batch  # noqa: F401,E402

@@ -1,0 +1,101 @@
+"""Stall-free batching (host logic, CPU): the iteration rules of the
+Sarathi-Serve digest's Algorithm 3 checked as invariants over whole runs."""
+import numpy as np
+import pytest
+
+from chunked_prefill_hybrid_rmsnorm_amd.scheduler import StallFreeScheduler
+
+
+def run(prompts, gen_len, budget):
+    s = StallFreeScheduler(prompts, gen_len, budget)
+    log = []
+    while True:
+        b = s.next_batch()
+        if b is None:
+            break
+        running_decoders = [r for r in s.running if s.reqs[r].prefill_done and r not in
+                            [c.rid for c in b.chunks]]
+        ctx = {r: s.decode_context(r) for r in b.decodes}
+        log.append((b, sorted(running_decoders), ctx))
+        s.commit(b)
+        assert len(log) < 10000
+    return s, log
+
+
+@pytest.mark.parametrize("prompts,gen_len,budget", [
+    ([5, 17, 30, 9, 12], 4, 16),
+    ([50, 500, 120, 7, 333, 64], 10, 128),
+    (list(np.random.default_rng(3).integers(50, 500, size=32)), 100, 512),
+])
+def test_iteration_rules(prompts, gen_len, budget):
+    s, log = run(prompts, gen_len, budget)
+    admitted = []
+    for b, decoders, ctx in log:
+        # every request past its prompt decodes in every iteration until done
+        assert sorted(b.decodes) == decoders
+        # the budget bounds the rows whenever the decodes alone fit in it
+        if len(b.decodes) <= budget:
+            assert b.n_rows <= budget
+        # new requests come in arrival order; at most one chunk continues a prompt
+        for c in b.chunks:
+            if c.start == 0 and c.rid not in admitted:
+                admitted.append(c.rid)
+        assert sum(1 for c in b.chunks if c.start > 0) <= 1
+        # decode rows sit at the position after the prompt and the earlier tokens
+        for r in b.decodes:
+            req = s.reqs[r]
+            assert ctx[r] >= req.prompt_len
+    assert admitted == list(range(len(prompts)))
+
+
+@pytest.mark.parametrize("prompts,gen_len,budget", [([5, 17, 30, 9, 12], 4, 16),
+                                                    ([50, 500, 120, 7], 10, 64)])
+def test_every_token_once_in_order(prompts, gen_len, budget):
+    s, log = run(prompts, gen_len, budget)
+    prefilled = {i: 0 for i in range(len(prompts))}
+    tokens = {i: [] for i in range(len(prompts))}
+    for b, _, _ in log:
+        for c in b.chunks:
+            # each prompt is prefilled contiguously from its start
+            assert c.start == prefilled[c.rid]
+            prefilled[c.rid] += c.length
+        rows = b.n_rows
+        for row, rid, k in b.samples:
+            assert 0 <= row < rows
+            tokens[rid].append(k)
+    for i, p in enumerate(prompts):
+        assert prefilled[i] == p
+        assert tokens[i] == list(range(gen_len))
+    assert all(r.done for r in s.reqs)
+
+
+def test_chunk_sample_is_its_last_row_and_decodes_follow_chunks():
+    s = StallFreeScheduler([3, 4], 2, 16)
+    b = s.next_batch()
+    assert [(c.rid, c.start, c.length) for c in b.chunks] == [(0, 0, 3), (1, 0, 4)]
+    assert b.samples == [(2, 0, 0), (6, 1, 0)]
+    s.commit(b)
+    b = s.next_batch()
+    assert b.chunks == [] and b.decodes == [0, 1]
+    assert b.samples == [(0, 0, 1), (1, 1, 1)]
+    assert [s.decode_context(r) for r in b.decodes] == [3, 4]
+    s.commit(b)
+    assert s.next_batch() is None
+
+
+def test_long_prompt_is_chunked_beside_decodes():
+    # request 0 decodes while request 1's long prompt is cut to the budget left
+    s = StallFreeScheduler([2, 40], 5, 8)
+    b = s.next_batch()
+    assert [(c.rid, c.start, c.length) for c in b.chunks] == [(0, 0, 2), (1, 0, 6)]
+    s.commit(b)
+    b = s.next_batch()
+    assert b.decodes == [0] and [(c.rid, c.start, c.length) for c in b.chunks] == [(1, 6, 7)]
+    assert b.n_rows == 8
+
+
+def test_bad_arguments():
+    with pytest.raises(ValueError):
+        StallFreeScheduler([3, 0], 2, 16)
+    with pytest.raises(ValueError):
+        StallFreeScheduler([3], 2, 0)
