@@ -23,6 +23,7 @@
 // short contexts idle and load some compute units twice as much as others).
 // A decode that falls inside one slice is finished by its wave; otherwise
 // each slice leaves a partial result for the merge.
+#include <atomic>
 #include <string.h>
 
 #include "attn_common.h"
@@ -490,12 +491,15 @@ size_t decode_workspace_bytes(int n_decodes, int nq, int nkv, int d, int max_ctx
   return (size_t)nq * pn * (d + 2) * sizeof(float) + 256;
 }
 
-// Workgroups of attention_kernel<D> the device holds at once (cached per device).
+// Workgroups of attention_kernel<D> the device holds at once, cached per
+// device.  Host threads may race to fill an entry; each computes the same
+// value, and the atomic makes the store and the loads well defined.
 static int attention_slots(int d) {
-  static int cache[2][64];
+  static std::atomic<int> cache[2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int& c = cache[d == 128 ? 1 : 0][dev];
+  std::atomic<int>& slot = cache[d == 128 ? 1 : 0][dev];
+  int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -506,6 +510,7 @@ static int attention_slots(int d) {
                                   &per_cu, attention_kernel<64>, 64 * kAttnWaves, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
     c = max(1, cus * per_cu);
+    slot.store(c, std::memory_order_relaxed);
   }
   return c;
 }

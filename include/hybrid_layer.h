@@ -27,8 +27,10 @@
  *  - bf16 values are passed as uint16_t bit patterns (hl_bf16);
  *  - every pointer to data is a DEVICE pointer owned by the caller unless
  *    stated otherwise; the library allocates nothing, frees nothing and keeps
- *    no pointer after it returns; it holds no mutable global state, so calls
- *    on different streams with different workspaces may run concurrently;
+ *    no pointer after it returns; its only global state is a per-device
+ *    cache of the attention kernel's occupancy, filled on first use and safe
+ *    to fill from several threads, so calls on different streams with
+ *    different workspaces may run concurrently;
  *  - calls only enqueue work on `stream` (0 = the null stream) and return;
  *    none synchronises except hl_validate_metadata;
  *  - return value: HL_OK (0) or a negative HL_ERR_* code; nothing is
