@@ -17,6 +17,33 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 // bank conflicts.  Wave w issues blocks w, w + NW, ...  Rows past the end of
 // A or W are clamped to the last valid row: their products only reach
 // outputs that are never stored.
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4), written as
+// inline asm.  The compiler models its own form of this copy as an LDS access
+// that may complete out of order with LDS reads, and then makes every LDS read
+// in the loop wait for all reads before it; hidden from it, the reads get
+// exact counts.  Completion of the copies is tracked by hand with vmcnt waits
+// and the workgroup barrier.  `lds` is wave-uniform; M0 carries it.
+__device__ __forceinline__ void lds_copy16(const bf16* src, char* lds) {
+  const uint32_t dst = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(dst)
+               : "memory");
+}
+
+// Instruction schedule of one stage's fragment reads and MFMAs: kLead LDS
+// reads, then after each group of FN MFMAs (one A fragment times the W
+// fragments) one more read while any remain.  An A fragment is thus read
+// kReadAhead groups before its MFMAs issue, so LDS latency hides behind them.
+constexpr int kReadAhead = 3;
+template <int GROUP, int NGROUPS, int EXTRA, int g = 0>
+__device__ __forceinline__ void sched_stream() {
+  if constexpr (g < NGROUPS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, GROUP, 0);  // MFMA
+    if constexpr (g < EXTRA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    sched_stream<GROUP, NGROUPS, EXTRA, g + 1>();
+  }
+}
+
 template <int BK>
 __device__ __forceinline__ int swz(int row, int chunk) {
   return BK == 64 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 2) & 3));
@@ -111,7 +138,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
     char* st = smem + (step % STAGES) * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i)
-      if (wave + i * NW < NBLK) lds_dma16(src[i] + kt * BK, st + (wave + i * NW) * 1024);
+      if (wave + i * NW < NBLK) lds_copy16(src[i] + kt * BK, st + (wave + i * NW) * 1024);
   };
   const bool more = (NBLK % NW) != 0 && wave < NBLK % NW;  // this wave copies PER_WAVE blocks
 
@@ -142,6 +169,14 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   }
   // fragment rows start at multiples of 16, so the swizzle depends on l16 only
 
+  constexpr int NSUB = BK / 32 / KG;  // 32-wide sub-steps per wave per stage
+  constexpr int kLead = NSUB * FN + kReadAhead < NSUB * (FN + FM) ? NSUB * FN + kReadAhead
+                                                                  : NSUB * (FN + FM);
+  // Kernel arguments read only after the loop arrive by scalar loads; such
+  // loads may complete out of order with LDS reads, so while one is pending
+  // every LDS wait in the loop would have to drain all reads.  Consume them
+  // here so the loop's waits count LDS reads alone.
+  asm volatile("" ::"s"(C), "s"(R), "s"(part), "s"(M), "s"(N));
   if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(s);
@@ -155,20 +190,31 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
       asm volatile("" ::: "memory");
       issue(it + STAGES - 1);
       const char* st = smem + (it % STAGES) * STAGE_BYTES;
+      // W fragments of every sub-step first, then the A fragments in the
+      // order the MFMA groups consume them; the schedule below keeps
+      // kReadAhead A reads in flight ahead of the group that needs them
+      bf16x8 af[NSUB][FN], bfr[NSUB][FM];
 #pragma unroll
-      for (int kk = 0; kk < BK / 32 / KG; ++kk) {
-        const int ks = kk * KG + kg;
-        bf16x8 af[FN], bfr[FM];
-        const int so = swz<BK>(l16, ks * 4 + q) << 4;
+      for (int kk = 0; kk < NSUB; ++kk) {
+        const int so = swz<BK>(l16, (kk * KG + kg) * 4 + q) << 4;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) af[fn] = as_bf16x8(ld16(st + w_off[fn] + so));
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) bfr[fm] = as_bf16x8(ld16(st + a_off[fm] + so));
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma16x16x32(af[fn], bfr[fm], acc[fn][fm]);
+        for (int fn = 0; fn < FN; ++fn) af[kk][fn] = as_bf16x8(ld16(st + w_off[fn] + so));
       }
+#pragma unroll
+      for (int kk = 0; kk < NSUB; ++kk) {
+        const int so = swz<BK>(l16, (kk * KG + kg) * 4 + q) << 4;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) bfr[kk][fm] = as_bf16x8(ld16(st + a_off[fm] + so));
+      }
+#pragma unroll
+      for (int kk = 0; kk < NSUB; ++kk)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fn][fm] = mfma16x16x32(af[kk][fn], bfr[kk][fm], acc[fn][fm]);
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // LDS reads
+      sched_stream<FN, NSUB * FM, NSUB * (FN + FM) - kLead>();
     }
   }
   wait_vmcnt<0>();  // drain the clamped tail copies before the workgroup ends
