@@ -346,12 +346,50 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) 
 
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the parts of one
 // (row, head), stored consecutively from `base`; lane i takes dims D/64 i ...
-// Parts are loaded 8 at a time (indices clamped to the last part), so their
-// load latencies overlap; they are summed in part order.
+// Up to 16 parts are loaded in one round; more are loaded 8 at a time
+// (indices clamped to the last part) in two passes.  Either way the parts are
+// summed in part order.
 template <int D>
 __device__ __forceinline__ void merge_unit(const float* __restrict__ o_part,
                                            const float* __restrict__ ml_part, size_t base,
                                            int n_parts, bf16* __restrict__ orow) {
+  constexpr int PER = D / 64;
+  // up to 16 parts: every load in one round, then the sum from registers
+  // (n_parts is uniform over the block, so the guards are scalar branches)
+  constexpr int ONE = 16;
+  if (n_parts <= ONE) {
+    float mv[ONE], lv[ONE], ov[ONE][PER];
+#pragma unroll
+    for (int u = 0; u < ONE; ++u) {
+      if (u < n_parts) {
+        const size_t pi = base + u;
+        mv[u] = ml_part[pi * 2];
+        lv[u] = ml_part[pi * 2 + 1];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ov[u][i] = o_part[pi * D + threadIdx.x * PER + i];
+      }
+    }
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < ONE; ++u)
+      if (u < n_parts) mmax = fmaxf(mmax, mv[u]);
+    float o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < ONE; ++u) {
+      if (u >= n_parts || mv[u] == -INFINITY) continue;  // no visible key in this part
+      const float w = exp2f(mv[u] - mmax);
+      lsum += w * lv[u];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += w * ov[u][i];
+    }
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) orow[threadIdx.x * PER + i] = f2bf(o[i] * inv);
+    return;
+  }
   constexpr int U = 8;
   float mmax = -INFINITY;
   for (int p0 = 0; p0 < n_parts; p0 += U) {
@@ -361,7 +399,6 @@ __device__ __forceinline__ void merge_unit(const float* __restrict__ o_part,
 #pragma unroll
     for (int u = 0; u < U; ++u) mmax = fmaxf(mmax, mv[u]);
   }
-  constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;

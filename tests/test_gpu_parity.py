@@ -153,6 +153,18 @@ def test_layer_edge_cases(name):
     check_layer(hb, gpu, run_oracle(hb))
 
 
+@pytest.mark.parametrize("shape", [TINY, D128], ids=["d64", "d128"])
+def test_merge_of_many_parts(shape):
+    """A 16-row chunk after 6000 cached tokens (about 21 key segments) beside a
+    4000-token decode (about 31 slices): rows with more parts than the merge
+    loads in one round take its two-pass path."""
+    _flush(f"merge of many parts, head dim {shape.head_dim}")
+    hb = make_hybrid_batch(shape, chunk_lens=[16], chunk_starts=[6000], ctx_lens=[4000, 9],
+                           seed=23, random_gains=True)
+    _, gpu = run_gpu(hb)
+    check_layer(hb, gpu, run_oracle(hb))
+
+
 @pytest.mark.parametrize("shape", [D128, G8], ids=["d128", "group8"])
 def test_layer_other_head_shapes(shape):
     hb = make_hybrid_batch(shape, chunk_lens=[40], chunk_starts=[30], n_decodes=3,
