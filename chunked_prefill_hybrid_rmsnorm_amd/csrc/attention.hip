@@ -58,6 +58,7 @@ struct AttnArgs {
   int dc_wgs;     // decode workgroups = ceil(dc_slices * nkv / 4)
   float* dc_o;
   float* dc_ml;
+  int merge_row0;  // first row the merge grid covers (chunk rows only when keys were split)
 };
 
 template <int D>
@@ -434,7 +435,7 @@ __device__ __forceinline__ void merge_unit(const float* __restrict__ o_part,
 // kernel.
 template <int D>
 __global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs A) {
-  const int h = blockIdx.x, r = blockIdx.y;
+  const int h = blockIdx.x, r = A.merge_row0 + blockIdx.y;
   bf16* orow = A.attn;
   if (r < A.chunks.n_rows) {
     if (A.pf_ns <= 1) return;
@@ -597,8 +598,11 @@ hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const Chunk
   }
   const int wgs = A.pf_wgs + A.dc_wgs;
   if (wgs == 0) return mid ? hipEventRecord(mid, s) : hipSuccess;
-  const int merge_rows = chunks.n_rows + dec.n;
-  const bool merge = A.pf_ns > 1 || A.dc_slices > 1;
+  // chunk rows need the merge only when their keys were split; decode rows
+  // whenever there is more than one slice
+  A.merge_row0 = A.pf_ns > 1 ? 0 : chunks.n_rows;
+  const int merge_rows = chunks.n_rows + dec.n - A.merge_row0;
+  const bool merge = (A.pf_ns > 1 || A.dc_slices > 1) && merge_rows > 0;
   if (d == 128)
     hipLaunchKernelGGL(attention_kernel<128>, dim3(wgs), dim3(64 * kAttnWaves), 0, s, A);
   else
