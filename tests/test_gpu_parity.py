@@ -142,6 +142,13 @@ EDGE = {
     # few chunk rows after a long prefix: the key range is split over workgroups and merged
     "long_prior_chunk_key_split": dict(chunk_lens=[40], chunk_starts=[1000], n_decodes=2),
     "two_long_chunks_key_split": dict(chunk_lens=[33, 7], chunk_starts=[700, 1500], ctx_lens=[31, 32]),
+    # the most chunks one call takes (HL_MAX_CHUNKS), ragged lengths and starts
+    "sixteen_chunks_max": dict(chunk_lens=[1, 2, 3, 5, 8, 13, 4, 7, 9, 2, 6, 11, 1, 3, 5, 16],
+                               chunk_starts=[0, 30, 7, 64, 3, 0, 90, 12, 40, 5, 77, 20, 130, 1, 9, 48],
+                               n_decodes=4),
+    # more decodes than one wave scans at a time (64): slice search and merge
+    # walk several 64-decode blocks
+    "many_decodes": dict(chunk_lens=[5], chunk_starts=[3], n_decodes=150, ctx_range=(0, 70)),
 }
 
 
