@@ -233,6 +233,64 @@ def stored_traffic(path: str, slot: str) -> Optional[float]:
     return e.get("traffic_bytes") if e else None
 
 
+# MFMA utilisation from one rocprofv3 --pmc pass with these four counters.
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4  # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8         # GRBM_GUI_ACTIVE counts each XCD's active cycles
+
+
+def mfma_summary(counter_csv: str, trace_csv: Optional[str] = None, skip: int = 0) -> dict:
+    """Per slot: bf16 MFMA flops counted by the hardware (MOPS are units of
+    512 flops), MFMA busy cycles summed over all SIMDs, the kernel's active
+    cycles per XCD, and from them the MFMA pipe utilisation
+    busy / (SIMDS * active cycles per XCD).  With a kernel trace, also the
+    counted flops over the traced average duration, against 2.5 PFLOP/s."""
+    vals = {c: counter_values(counter_csv, c)[0] for c in MFMA_COUNTERS}
+    durs = kernel_durations(trace_csv, skip) if trace_csv else {}
+    out = {}
+    for s in SLOTS:
+        if s not in vals[MFMA_COUNTERS[0]]:
+            continue
+        mops, busy, _, active = (_mean(vals[c].get(s, [])) for c in MFMA_COUNTERS)
+        if mops <= 0:
+            continue
+        e = {"flops": mops * 512, "busy_cycles": busy, "active_cycles_per_xcd": active / XCDS}
+        e["mfma_util"] = busy / (SIMDS * e["active_cycles_per_xcd"]) if active else None
+        if s in durs and durs[s]:
+            t = _mean(durs[s]) / 1e9
+            e["trace_us"] = t * 1e6
+            e["tflops"] = e["flops"] / t / 1e12
+            e["frac_of_peak"] = e["flops"] / t / 2.5e15
+        out[s] = e
+    return out
+
+
+def write_mfma_markdown(path: str, res: dict, workload: str, commands: List[str]) -> None:
+    lines = [f"# MFMA utilisation per kernel, {workload}", "", "Commands (run from the repository root):",
+             ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", f"Kernel sources digest: `{source_hash()}`", "",
+              "Counted flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. MFMA util = SQ_VALU_MFMA_BUSY_CYCLES "
+              f"(summed over the {SIMDS} SIMDs) / ({SIMDS} x GRBM_GUI_ACTIVE / {XCDS}), i.e. the share "
+              "of the kernel's cycles each SIMD's matrix pipe was busy. In a counter pass the active "
+              "cycles span the whole serialised dispatch, start-up included, so for short kernels "
+              "this is a lower bound. Trace columns use the kernel trace's average duration; frac of "
+              "peak is the counted flops over that duration against 2.5 PFLOP/s dense bf16.", "",
+              "| slot | counted GFLOP | MFMA busy Mcycles | active kcycles / XCD | MFMA util | trace us "
+              "| TFLOP/s | frac of peak |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for s, e in res.items():
+        def f(k, fmt):
+            return format(e[k], fmt) if e.get(k) is not None else "-"
+        lines.append(f"| {s} | {e['flops'] / 1e9:.2f} | {e['busy_cycles'] / 1e6:.2f} | "
+                     f"{e['active_cycles_per_xcd'] / 1e3:.1f} | {f('mfma_util', '.3f')} | "
+                     f"{f('trace_us', '.2f')} | {f('tflops', '.0f')} | {f('frac_of_peak', '.3f')} |")
+    lines.append("")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--trace")
@@ -244,7 +302,15 @@ def main():
     p.add_argument("--traffic")
     p.add_argument("--skip", type=int, default=0,
                    help="drop the first N dispatches of each slot (clock ramp)")
+    p.add_argument("--mfma", help="counter CSV of a pass over MFMA_COUNTERS")
+    p.add_argument("--mfma-md")
     a = p.parse_args()
+    if a.mfma:
+        res = mfma_summary(a.mfma, a.trace, a.skip)
+        if a.mfma_md:
+            write_mfma_markdown(a.mfma_md, res, a.workload, a.command)
+        print(json.dumps(res, indent=1))
+        return
     res = summarize(a.trace, a.fetch, a.write, a.skip)
     if a.md:
         write_markdown(a.md, res, a.workload, a.command)

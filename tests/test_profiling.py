@@ -42,3 +42,26 @@ def test_foreign_kernels_are_skipped():
     lab = SlotLabeler()
     assert lab.label("__amd_rocclr_copyBuffer") is None
     assert lab.label("void at::native::vectorized_elementwise_kernel<16>(int)") is None
+
+
+def test_mfma_summary_from_counter_rows(tmp_path):
+    """Four counters of one gate/up dispatch: flops are MOPS x 512, the
+    utilisation is busy cycles over SIMDs x per-XCD active cycles."""
+    import csv
+    from chunked_prefill_hybrid_rmsnorm_amd.profiling import MFMA_COUNTERS, SIMDS, XCDS, mfma_summary
+    path = tmp_path / "m_counter_collection.csv"
+    vals = {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 1000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 500.0,
+            "SQ_BUSY_CU_CYCLES": 7.0, "GRBM_GUI_ACTIVE": 8.0 * 2.0}
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, k in enumerate(SPLIT_CALL[:8]):
+            for c in MFMA_COUNTERS:
+                v = vals[c] if "gemm_dma_kernel<288, 128, 2, 4, 2" in k else 0.0
+                w.writerow([i + 1, k, c, v])
+    res = mfma_summary(str(path))
+    assert list(res) == ["gemm_gate_up"]
+    e = res["gemm_gate_up"]
+    assert e["flops"] == 1000.0 * 512
+    assert e["active_cycles_per_xcd"] == 2.0 and XCDS == 8
+    assert abs(e["mfma_util"] - 500.0 / (SIMDS * 2.0)) < 1e-12
