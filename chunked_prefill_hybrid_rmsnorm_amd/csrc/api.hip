@@ -23,6 +23,11 @@ int check_config(const hl_config* c) {
   if (c->n_q_heads % c->n_kv_heads) return HL_ERR_SHAPE;
   if (c->n_q_heads / c->n_kv_heads > 16) return HL_ERR_UNSUPPORTED;
   if (c->hidden % 64 || c->ffn % 64 || (c->n_q_heads * c->head_dim) % 64) return HL_ERR_SHAPE;
+  // the GEMM copies address each weight matrix by 32-bit byte offsets
+  const size_t nqkv = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+  if (std::max({nqkv, (size_t)c->ffn, (size_t)c->n_q_heads * c->head_dim}) * c->hidden * 2 >
+      UINT32_MAX)
+    return HL_ERR_UNSUPPORTED;
   return HL_OK;
 }
 

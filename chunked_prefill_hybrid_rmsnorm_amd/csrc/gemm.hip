@@ -232,11 +232,14 @@ static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, con
       return run_gemm_dma<288, 96, 2, 2, EPI, 3, 64, 2>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
   }
   if (ch.big) {
+    // the 128-column tiles run the two waves of a SIMD half a k-step apart
+    // (ping-pong); the 96-column tile, whose k loops are short, does not gain
+    // from it.
     // long k loops amortise the k-group reduction: 4 waves per group, each
     // with a 144 x 64 sub-tile (fewer LDS bytes per MFMA)
     if ((k / kGemmBK) / ch.splits >= 48)
-      return run_gemm_dma<288, 128, 2, 2, EPI, 3, 64, 2>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
-    return run_gemm_dma<288, 128, 2, 4, EPI, 3>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+      return run_gemm_dma<288, 128, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+    return run_gemm_dma<288, 128, 2, 4, EPI, 3, 64, 1, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
   }
   return run_gemm_dma<128, 128, 2, 2, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
 }

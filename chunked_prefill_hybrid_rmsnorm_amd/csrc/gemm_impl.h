@@ -14,19 +14,21 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 // values of K per row, i.e. 8 or 4 chunks of 16 B; one copy instruction fills
 // 1 KB = 8 or 16 rows.  Chunk c of row r sits in slot c ^ (r % 8) (BK 64) or
 // c ^ ((r / 4) % 4) (BK 32), which keeps the 16-row fragment reads free of
-// bank conflicts.  Wave w issues blocks w, w + NW, ...  Rows past the end of
-// A or W are clamped to the last valid row: their products only reach
-// outputs that are never stored.
-// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4), written as
-// inline asm.  The compiler models its own form of this copy as an LDS access
-// that may complete out of order with LDS reads, and then makes every LDS read
-// in the loop wait for all reads before it; hidden from it, the reads get
-// exact counts.  Completion of the copies is tracked by hand with vmcnt waits
-// and the workgroup barrier.  `lds` is wave-uniform; M0 carries it.
-__device__ __forceinline__ void lds_copy16(const bf16* src, char* lds) {
+// bank conflicts.  Copying wave w issues blocks w, w + NCW, ...  Rows past
+// the end of A or W are clamped to the last valid row: their products only
+// reach outputs that are never stored.
+// 16-byte global -> LDS copy per lane, written as inline asm.  The compiler
+// models its own form of this copy as an LDS access that may complete out of
+// order with LDS reads, and then makes every LDS read in the loop wait for
+// all reads before it; hidden from it, the reads get exact counts.
+// Completion of the copies is tracked by hand with vmcnt waits and the
+// workgroup barrier.  The address is a scalar base plus a per-lane 32-bit
+// byte offset (the instruction's saddr form: one VGPR per copy instead of
+// two).  `lds` is wave-uniform; M0 carries it.
+__device__ __forceinline__ void lds_copy16(const bf16* base, uint32_t voff, char* lds) {
   const uint32_t dst = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
-               "s"(dst)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(base), "s"(dst)
                : "memory");
 }
 
@@ -54,7 +56,18 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // sub-tile, so fewer LDS bytes are read per MFMA, while the workgroup still
 // holds two waves per SIMD.  The groups' partial tiles are summed through LDS
 // at the end, each group finishing half of the row fragments.
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1>
+//
+// PP (ping-pong): the two waves that share a SIMD (wave w and w + NW/2) work
+// half a k-step apart, so one reads fragments from LDS while the other keeps
+// the SIMD's matrix pipe busy.  Each k-step has two workgroup barriers:
+//   slot 1: first half copies stage it+2 and reads stage it; second half
+//           multiplies stage it-1
+//   slot 2: first half multiplies stage it and waits for its copies of stage
+//           it+1; second half reads stage it
+// Only the first half issues copies, so its own vmcnt waits plus the barrier
+// cover every copy.  Every wave passes the same barriers (1 + 2 per k-step).
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1,
+          bool PP = false>
 __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W2,
     bf16* __restrict__ C, const bf16* __restrict__ R, float* __restrict__ part, int M, int Mp,
@@ -70,15 +83,18 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
   constexpr int A_BLK = BM / BLK_ROWS, W_BLK = BN / BLK_ROWS;  // 1 KB blocks per stage
   constexpr int NBLK = A_BLK + W_BLK;
-  // copy instructions per wave per stage: the first NBLK % NW waves take one more
-  constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
-  constexpr int PER_WAVE_LO = NBLK / NW;
+  constexpr int NCW = PP ? NW / 2 : NW;  // waves that issue copies
+  // copy instructions per copying wave per stage: the first NBLK % NCW take one more
+  constexpr int PER_WAVE = (NBLK + NCW - 1) / NCW;
+  constexpr int PER_WAVE_LO = NBLK / NCW;
   constexpr int STAGE_BYTES = NBLK * 1024;
   static_assert(BM % BLK_ROWS == 0 && BN % BLK_ROWS == 0, "tiles are whole copy blocks");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole MFMA blocks");
   static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && (BN / 2) % BLK_ROWS == 0), "swiglu pairing");
   static_assert(STAGES >= 3, "need at least three stages");
   static_assert(PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(!PP || (STAGES == 3 && NW % 2 == 0 && NBLK % NCW == 0),
+                "ping-pong: three stages, equal copy shares");
   static_assert(KG == 1 || KG == BK / 32, "a k-group takes one 32-wide slice of a stage");
   static_assert(KG == 1 || NWG * FM * FN * 1024 <= STAGES * STAGE_BYTES, "reduction fits the ring");
 
@@ -107,40 +123,41 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   const int wm = wl / WN, wn = wl % WN;
   const int l16 = lane & 15, q = lane >> 4;
 
-  // per-lane source row pointers of this wave's copy blocks (k offset added per stage)
-  const bf16* src[PER_WAVE];
+  // Per-lane byte offsets of this wave's copy blocks from their matrix's base
+  // (A, W or W2, uniform per block since a block never straddles two); the
+  // k offset is added to the scalar base per stage.  32-bit offsets keep one
+  // VGPR per block (matrices here are far below 4 GiB; the host checks).
+  uint32_t voff[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int blk = min(wave + i * NW, NBLK - 1);
+    const int blk = min(wave + i * NCW, NBLK - 1);
     const int row = blk * BLK_ROWS + lane / NCH;
     const int chunk = swz<BK>(row, lane % NCH);
-    const bf16* p;
+    size_t r;
     if (blk < A_BLK) {
-      const int m = min(m0 + row, Mp - 1);
-      p = A + (size_t)m * K;
+      r = (size_t)min(m0 + row, Mp - 1);
     } else {
       const int wr = row - BM;
-      const bf16* base = W;
-      int n;
-      if (EPI == EPI_SWIGLU) {
-        const bool up = wr >= BN / 2;
-        base = up ? W2 : W;
-        n = n0 + (up ? wr - BN / 2 : wr);
-      } else {
-        n = n0 + wr;
-      }
-      p = base + (size_t)min(n, N - 1) * K;
+      const int n = EPI == EPI_SWIGLU && wr >= BN / 2 ? n0 + wr - BN / 2 : n0 + wr;
+      r = (size_t)min(n, N - 1);
     }
-    src[i] = p + chunk * 8;
+    voff[i] = (uint32_t)((r * K + chunk * 8) * sizeof(bf16));
   }
+  auto block_base = [&](int blk) -> const bf16* {  // wave-uniform
+    if (blk < A_BLK) return A;
+    if (EPI == EPI_SWIGLU && (blk - A_BLK) * BLK_ROWS >= BN / 2) return W2;
+    return W;
+  };
   auto issue = [&](int step) {  // copy k-step `step` (clamped) into its ring slot
     const int kt = kt0 + min(step, max(nk - 1, 0));
     char* st = smem + (step % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      if (wave + i * NW < NBLK) lds_copy16(src[i] + kt * BK, st + (wave + i * NW) * 1024);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int blk = wave + i * NCW;
+      if (blk < NBLK) lds_copy16(block_base(blk) + (size_t)kt * BK, voff[i], st + blk * 1024);
+    }
   };
-  const bool more = (NBLK % NW) != 0 && wave < NBLK % NW;  // this wave copies PER_WAVE blocks
+  const bool more = (NBLK % NCW) != 0 && wave < NBLK % NCW;  // this wave copies PER_WAVE blocks
 
   f32x4 acc[FN][FM];
 #pragma unroll
@@ -177,7 +194,69 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   // every LDS wait in the loop would have to drain all reads.  Consume them
   // here so the loop's waits count LDS reads alone.
   asm volatile("" ::"s"(C), "s"(R), "s"(part), "s"(M), "s"(N));
-  if (nk > 0) {
+  if constexpr (PP) {
+    // fragments live across the slot boundary (second half: across the k-step)
+    bf16x8 af[NSUB][FN], bfr[NSUB][FM];
+    const bool first = wave < NCW;
+    auto read_frags = [&](const char* st) {
+#pragma unroll
+      for (int kk = 0; kk < NSUB; ++kk) {
+        const int so = swz<BK>(l16, (kk * KG + kg) * 4 + q) << 4;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) af[kk][fn] = as_bf16x8(ld16(st + w_off[fn] + so));
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) bfr[kk][fm] = as_bf16x8(ld16(st + a_off[fm] + so));
+      }
+      // the reads must have landed before the barrier: the stage is
+      // overwritten by copies issued after a later one
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    };
+    auto multiply = [&]() {
+#pragma unroll
+      for (int kk = 0; kk < NSUB; ++kk)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fn][fm] = mfma16x16x32(af[kk][fn], bfr[kk][fm], acc[fn][fm]);
+    };
+    auto barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // the two halves run separate loops (clear register lifetimes), with the
+    // same barrier count: 1 + 2 nk
+    if (nk > 0 && first) {
+      issue(0);
+      issue(1);
+      wait_vmcnt<PER_WAVE>();  // stage 0 landed
+      barrier();
+      for (int it = 0; it < nk; ++it) {
+        issue(it + 2);  // into the slot of stage it-1, read by everyone before the last barrier
+        read_frags(smem + (it % STAGES) * STAGE_BYTES);
+        barrier();
+        multiply();  // stage it
+        __builtin_amdgcn_sched_barrier(0);  // every MFMA issues before the wait
+        wait_vmcnt<PER_WAVE>();  // stage it+1 landed; stage it+2 may be in flight
+        barrier();
+      }
+    } else if (nk > 0) {
+      barrier();
+      barrier();
+      read_frags(smem);  // stage 0
+      barrier();
+      for (int it = 1; it < nk; ++it) {
+        multiply();  // stage it-1
+        barrier();
+        read_frags(smem + (it % STAGES) * STAGE_BYTES);
+        barrier();
+      }
+      multiply();  // stage nk-1
+    }
+  } else if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(s);
     for (int it = 0; it < nk; ++it) {
@@ -303,14 +382,18 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1>
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES, int BK = 64, int KG = 1,
+          bool PP = false>
 hipError_t run_gemm_dma(const bf16* a, const bf16* w, const bf16* w2, bf16* c, const bf16* r,
                         float* part, int m, int mp, int n, int k, int splits, hipStream_t s) {
   constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
   constexpr size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
   static_assert(lds <= 160 * 1024, "LDS budget");
+  // the copies address A and W by 32-bit byte offsets
+  if ((size_t)mp * k * sizeof(bf16) > UINT32_MAX || (size_t)n * k * sizeof(bf16) > UINT32_MAX)
+    return hipErrorInvalidValue;
   const int mt = (mp + BM - 1) / BM, nt = (n + OUT_N - 1) / OUT_N;
-  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK, KG>;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, EPI, STAGES, BK, KG, PP>;
   // raise the dynamic LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

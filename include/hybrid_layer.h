@@ -50,7 +50,8 @@ extern "C" {
 #define HL_OK 0
 #define HL_ERR_NULL (-1)        /* a required pointer is NULL */
 #define HL_ERR_SHAPE (-2)       /* sizes inconsistent or not multiples the kernels need */
-#define HL_ERR_UNSUPPORTED (-3) /* head_dim not 64/128, page_size not 16, too many chunks */
+#define HL_ERR_UNSUPPORTED (-3) /* head_dim not 64/128, page_size not 16, too many chunks,
+                                   a weight matrix of 4 GiB or more */
 #define HL_ERR_WORKSPACE (-4)   /* ws_bytes smaller than hl_workspace_bytes() */
 #define HL_ERR_LAUNCH (-5)      /* a kernel launch failed (hipGetLastError) */
 #define HL_ERR_METADATA (-6)    /* hl_validate_metadata found a bad table entry */

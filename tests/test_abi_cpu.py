@@ -72,6 +72,8 @@ def _cfg(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=96), -3), (dict(page_size=32), -3), (dict(n_kv_heads=3), -2),
     (dict(hidden=100), -2), (dict(ffn=1000), -2), (dict(n_q_heads=32, n_kv_heads=1), -3),
+    # a weight matrix of 4 GiB or more (the GEMM copies use 32-bit byte offsets)
+    (dict(hidden=65536, ffn=32768), -3),
 ])
 def test_config_errors(lib, kw, code):
     out = ctypes.c_size_t(0)
