@@ -12,6 +12,11 @@ using namespace hl;
 namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The GEMM copies address A and W by 32-bit byte offsets.
+bool gemm_fits_offsets(int m_padded, int n, int k) {
+  return (size_t)std::max(m_padded, n) * k * 2 <= UINT32_MAX;
+}
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 int check_config(const hl_config* c) {
@@ -362,6 +367,7 @@ int hl_gemm_bf16(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* 
   if (!a || !w || !c) return HL_ERR_NULL;
   if (m < 0 || m_padded < m || m_padded % 16 || n <= 0 || n % 64 || k <= 0 || k % 64)
     return HL_ERR_SHAPE;
+  if (!gemm_fits_offsets(m_padded, n, k)) return HL_ERR_UNSUPPORTED;
   const GemmEpilogue epi = residual ? EPI_RESIDUAL : EPI_STORE;
   const size_t need = gemm_workspace_bytes(epi, m_padded, n, k);
   if (ws && ws_bytes < need) return HL_ERR_WORKSPACE;
@@ -377,6 +383,7 @@ int hl_gemm_swiglu(const hl_bf16* a, const hl_bf16* w_gate, const hl_bf16* w_up,
                    int32_t m_padded, int32_t f, int32_t k, hipStream_t stream) {
   if (!a || !w_gate || !w_up || !act) return HL_ERR_NULL;
   if (m_padded < 0 || m_padded % 16 || f <= 0 || f % 64 || k <= 0 || k % 64) return HL_ERR_SHAPE;
+  if (!gemm_fits_offsets(m_padded, f, k)) return HL_ERR_UNSUPPORTED;
   return launch_gemm(EPI_SWIGLU, reinterpret_cast<const bf16*>(a),
                      reinterpret_cast<const bf16*>(w_gate), reinterpret_cast<const bf16*>(w_up),
                      reinterpret_cast<bf16*>(act), nullptr, nullptr, m_padded, m_padded, f, k,

@@ -194,7 +194,8 @@ int hl_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
  * k multiple of 64, n multiple of 64, m_padded multiple of 16.  ws (device,
  * 16-byte aligned, ws_bytes >= hl_gemm_workspace_bytes) lets the kernel split
  * K over more workgroups; with ws == NULL K is not split (same results up to
- * fp32 summation order). */
+ * fp32 summation order).  HL_ERR_UNSUPPORTED when a or w spans 4 GiB or more
+ * (max(m_padded, n) * k * 2 bytes). */
 int hl_gemm_bf16(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
                  int32_t m, int32_t m_padded, int32_t n, int32_t k, void* ws, size_t ws_bytes,
                  hipStream_t stream);
@@ -202,7 +203,8 @@ int hl_gemm_workspace_bytes(int32_t m_padded, int32_t n, int32_t k, size_t* byte
 
 /* act[m, f] = silu(sum_k a[m,k] w_gate[f,k]) * sum_k a[m,k] w_up[f,k] for
  * m < m_padded; silu(z) = z / (1 + exp(-z)).  a [m_padded, k],
- * w_gate/w_up [f, k], act [m_padded, f]. */
+ * w_gate/w_up [f, k], act [m_padded, f].  HL_ERR_UNSUPPORTED when a or a
+ * weight spans 4 GiB or more. */
 int hl_gemm_swiglu(const hl_bf16* a, const hl_bf16* w_gate, const hl_bf16* w_up, hl_bf16* act,
                    int32_t m_padded, int32_t f, int32_t k, hipStream_t stream);
 

@@ -122,6 +122,19 @@ def test_layer_forward_rejects_before_launch(lib):
              ctypes.byref(kv), fake + 4096, fake, 1 << 30, 16, None, None) == -1
 
 
+def test_gemm_entries_reject_before_launch(lib):
+    """Shape errors and operands of 4 GiB or more come back before any launch
+    (fake device pointers, no GPU needed)."""
+    fake = ctypes.c_void_p(0x1000)
+    g = lib.hl_gemm_bf16
+    assert g(fake, fake, fake, None, 16, 16, 100, 64, None, 0, None) == -2   # n % 64
+    assert g(fake, fake, fake, None, 16, 16, 65536, 65536, None, 0, None) == -3  # w: 8 GiB
+    assert g(fake, fake, fake, None, 65536, 65536, 64, 65536, None, 0, None) == -3  # a: 8 GiB
+    s = lib.hl_gemm_swiglu
+    assert s(fake, fake, fake, fake, 16, 65536, 65536, None) == -3
+    assert s(None, fake, fake, fake, 16, 64, 64, None) == -1
+
+
 def test_kv_layout_roundtrip():
     import numpy as np
     rng = np.random.default_rng(0)

@@ -72,7 +72,12 @@ def test_rmsnorm_step():
                                             (288, 288, 6144, 4096, True),
                                             (1, 16, 256, 1024, False),
                                             (257, 272, 4096, 14336, False),
-                                            (257, 272, 4096, 14336, True)])
+                                            (257, 272, 4096, 14336, True),
+                                            # 288-row ping-pong tile with one k-step, and
+                                            # with two splits of 8 k-steps; ragged last
+                                            # column tile
+                                            (200, 208, 320, 64, False),
+                                            (150, 160, 320, 1024, True)])
 def test_gemm_step(m, mp, n, k, split):
     """Without a workspace K is not split (one launch, the long-k tile with two
     k-groups for the 288-row shapes); with one the partials are reduced."""
