@@ -30,9 +30,11 @@
 
 namespace hl {
 
-constexpr int kAttnWaves = 4;
-constexpr int kPfRowsPerWave = 32;                       // two 16-row MFMA blocks
-constexpr int kPrefillRows = kPfRowsPerWave * kAttnWaves;  // rows per prefill workgroup
+// Waves per workgroup, a template parameter of the kernel: 8 (a prefill
+// workgroup is two groups of four waves on the same rows) or 4 (one group).
+constexpr int kPfHalfWaves = 4;  // waves of one prefill group
+constexpr int kPfRowsPerWave = 32;                         // two 16-row MFMA blocks
+constexpr int kPrefillRows = kPfRowsPerWave * kPfHalfWaves;  // rows per prefill workgroup
 constexpr int kPfStages = 3;                             // LDS ring depth of prefill K/V
 constexpr int kDecMinSliceSteps = 4;   // fewest 32-key steps in a decode slice
 constexpr int kDecMaxWaves = 4096;     // decode waves of one launch, all kv heads
@@ -80,7 +82,7 @@ struct PfStage {
   static constexpr int PAGE = 16 * D * 2;     // bytes of one page of one kv head
   static constexpr int BYTES = 4 * PAGE;      // K and V of two pages
   static constexpr int COPIES = BYTES / 1024;  // 1 KB copy instructions per step
-  static constexpr int PER_WAVE = COPIES / kAttnWaves;
+  static constexpr int PER_WAVE = COPIES / kPfHalfWaves;  // copies per wave of one group
 };
 
 __device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
@@ -128,15 +130,36 @@ __device__ __forceinline__ void prefill_frags(KvFrag<D>& f, const char* stage, i
   }
 }
 
+// Merge the (m, l, o) of the same rows over another key range into `a`
+// (base-2 scaled maxima; a part with m = -inf has seen no key).
+template <int D>
+__device__ __forceinline__ void merge_acc(AttnAcc<D>& a, float m1, float l1, const f32x4* o1) {
+  const float m = fmaxf(a.m, m1);
+  if (m == -INFINITY) return;  // neither part has a key for this row
+  const float f0 = a.m == -INFINITY ? 0.f : fast_exp2(a.m - m);
+  const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
+  a.m = m;
+  a.l = a.l * f0 + l1 * f1;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) a.o[i] = a.o[i] * f0 + o1[i] * f1;
+}
+
 // A prefill workgroup: 128 GQA rows (row = token * G + head) of one chunk and
 // one kv head, 32 per wave as two 16-row MFMA blocks, over one key segment.
-// The waves copy each 32-key step's K/V pages into an LDS ring together
-// (global -> LDS, kPfStages deep) and all read it from there, so a K/V byte
-// crosses the L2 -> CU path once per 128 rows.
-template <int D>
-__device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave, int lane,
-                                              char* ring) {
+// With eight waves (NW = 8) they form two groups of four on the same rows:
+// group 0 takes the first half of the segment's 32-key steps, group 1 the
+// rest, so every SIMD holds two waves of the workgroup.  Each group copies its steps' K/V pages into its own LDS
+// ring (global -> LDS, kPfStages deep) and reads them from there, so a K/V
+// byte crosses the L2 -> CU path once per 128 rows.  At the end group 1 hands
+// its (m, l, o) to group 0 through LDS, which merges and stores the rows.
+template <int D, int NW>
+__device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave_id, int lane,
+                                              char* ring_all) {
+  static_assert(NW == kPfHalfWaves || NW == 2 * kPfHalfWaves, "one or two wave groups");
+  constexpr int NGROUPS = NW / kPfHalfWaves;
   const int l16 = lane & 15, q = lane >> 4;
+  const int half = wave_id / kPfHalfWaves, wave = wave_id % kPfHalfWaves;
+  char* ring = ring_all + half * kPfStages * PfStage<D>::BYTES;
   const int per_chunk = A.pf_gx * A.pf_ns * A.nkv;
   const int c = b / per_chunk;
   const int rem = b % per_chunk;
@@ -179,18 +202,25 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   const int lim_min[2] = {wave_min(row_limit[0]), wave_min(row_limit[1])};
 
   const int blk_end = (k1 + 15) >> 4;
-  PageWindow win;
-  win.fill(ch.block_table, ch.n_blocks, k0 >> 4, blk_end, A.kv.num_pages, lane);
   const int nsteps = (k1 - k0 + 31) / 32;
+  // the group's steps: [s0, s0 + my_n); group 0 takes the larger half, and
+  // both groups run n_iter iterations (one barrier each)
+  const int n_iter = (nsteps + NGROUPS - 1) / NGROUPS;
+  const int s0 = half ? n_iter : 0;
+  const int my_n = half ? nsteps - n_iter : n_iter;
+  const int kg0 = k0 + s0 * 32;  // first key of the group
+  PageWindow win;
+  win.fill(ch.block_table, ch.n_blocks, kg0 >> 4, blk_end, A.kv.num_pages, lane);
   // keys from block blk_end on are read from a stand-in page: zero their V
   const int v_end = min(kv_len, blk_end * 16);
-  // copies of step s (pages past the table read page 0, whose keys are
-  // masked); every wave issues the same copies, and none past the last step
-  auto issue = [&](int s) {
-    const int t = k0 + min(s, nsteps - 1) * 32;
+  // copies of the group's step i (pages past the table read page 0, whose
+  // keys are masked); every wave of the group issues its share of the same
+  // copies, and none past the group's last step
+  auto issue = [&](int i) {
+    const int t = kg0 + i * 32;
     int p0 = win.at(t, ch.block_table, ch.n_blocks, blk_end, A.kv.num_pages, lane);
     int p1 = win.at(t + 16, ch.block_table, ch.n_blocks, blk_end, A.kv.num_pages, lane);
-    prefill_copy<D>(ring + (s % kPfStages) * PfStage<D>::BYTES, A.kv, g, max(p0, 0), max(p1, 0),
+    prefill_copy<D>(ring + (i % kPfStages) * PfStage<D>::BYTES, A.kv, g, max(p0, 0), max(p1, 0),
                     wave, lane);
   };
 
@@ -199,23 +229,54 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   init_acc<D>(a[1]);
   const float scale = kAttnLog2e * rsqrtf((float)D);
   static_assert(kPfStages == 3, "the waits below count one step in flight behind the current");
-  issue(0);
-  if (nsteps > 1) issue(1);
-  for (int i = 0; i < nsteps; ++i) {
+  if (my_n > 0) issue(0);
+  if (my_n > 1) issue(1);
+  for (int i = 0; i < n_iter; ++i) {
     // this step's copies have landed (the next step's may still be in flight)
-    if (i + 1 < nsteps)
+    if (i + 1 < my_n)
       wait_vmcnt<PfStage<D>::PER_WAVE>();
     else
       wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (i + 2 < nsteps) issue(i + 2);
-    if (!busy) continue;
+    if (i + 2 < my_n) issue(i + 2);
+    if (!busy || i >= my_n) continue;
     KvFrag<D> f;
     prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
-    const int t0 = k0 + i * 32;
+    const int t0 = kg0 + i * 32;
     compute_step<D, 2>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale, q);
+  }
+  // group 1 hands its rows' (m, l, o) to group 0 through the rings' LDS:
+  // per wave and row block, D/4 + 2 floats per lane, lane-minor
+  constexpr int XF = D / 4 + 2;
+  static_assert(NGROUPS == 1 || kPfHalfWaves * 2 * XF * 64 * 4 <= 2 * kPfStages * PfStage<D>::BYTES,
+                "exchange fits the rings");
+  float* xbuf = reinterpret_cast<float*>(ring_all) + (size_t)wave * 2 * XF * 64;
+  if (NGROUPS == 2) __syncthreads();  // every wave is done with both rings
+  if (NGROUPS == 2 && half == 1 && busy) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float* xr = xbuf + rb * XF * 64;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xr[(i * 4 + r) * 64 + lane] = a[rb].o[i][r];
+      xr[(D / 4) * 64 + lane] = a[rb].m;
+      xr[(D / 4 + 1) * 64 + lane] = a[rb].l;
+    }
+  }
+  if (NGROUPS == 2) __syncthreads();
+  if (half == 1 || !busy) return;
+#pragma unroll
+  for (int rb = 0; rb < 2 && NGROUPS == 2; ++rb) {
+    const float* xr = xbuf + rb * XF * 64;
+    f32x4 o1[D / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o1[i][r] = xr[(i * 4 + r) * 64 + lane];
+    merge_acc<D>(a[rb], xr[(D / 4) * 64 + lane], xr[(D / 4 + 1) * 64 + lane], o1);
   }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -330,9 +391,10 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int lan
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) {
-  __shared__ __attribute__((aligned(1024))) char ring[kPfStages * PfStage<D>::BYTES];
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs A) {
+  __shared__ __attribute__((aligned(1024)))
+  char ring[NW / kPfHalfWaves * kPfStages * PfStage<D>::BYTES];
   // the wave index is uniform across the wave: keep it (and everything derived
   // from it: work unit, key range, loop bounds) in scalar registers, so that
   // the loops branch on scalars instead of masking lanes
@@ -340,9 +402,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(AttnArgs A) 
   const int l16 = lane & 15, q = lane >> 4;
   const int b = blockIdx.x;
   if (b < A.pf_wgs)
-    prefill_block<D>(A, b, wave, lane, ring);
+    prefill_block<D, NW>(A, b, wave, lane, ring);
   else
-    decode_wave<D>(A, (b - A.pf_wgs) * kAttnWaves + wave, lane, l16, q);
+    decode_wave<D>(A, (b - A.pf_wgs) * NW + wave, lane, l16, q);
 }
 
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the parts of one
@@ -466,13 +528,17 @@ __global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs A) {
 }
 
 // ---------------------------------------------------------------- host side
-// Prefill key split: only when the chunk rows give few workgroups, into
-// segments of >= 256 keys (multiples of 32).  Prefill alone aims at ~512
-// workgroups (split below 256).  Beside decodes it aims at 128 (split below
-// 128): there the decode waves set the kernel time, every prefill workgroup
-// takes a slot a decode wave group could use, and every split adds partials
-// for the merge to read.
-constexpr int kPfAimAlone = 512, kPfAimHybrid = 128;
+// Prefill key split over workgroups: only when the chunk rows give few
+// workgroups, into segments of >= 256 keys (multiples of 32); each workgroup
+// splits its segment once more between its two wave groups.  Prefill alone
+// aims at ~256 workgroups, one per CU (split below 128).  Beside decodes it
+// aims at 64 (split below 64): there the decode waves set the kernel time,
+// every prefill workgroup takes a slot a decode wave group could use, and
+// every split adds partials for the merge to read.
+constexpr int kPfAimAlone = 256, kPfAimHybrid = 64;
+// 128-row groups (over all kv heads) from which a chunk beside decodes runs
+// in four-wave workgroups
+constexpr int kPfFourWaveFrom = 256;
 
 void prefill_split(const ChunkList& chunks, int nq, int nkv, bool with_decodes, int* nsplit,
                    int* seg) {
@@ -529,28 +595,80 @@ size_t decode_workspace_bytes(int n_decodes, int nq, int nkv, int d, int max_ctx
   return (size_t)nq * pn * (d + 2) * sizeof(float) + 256;
 }
 
-// Workgroups of attention_kernel<D> the device holds at once, cached per
+// Workgroups of attention_kernel<D, NW> the device holds at once, cached per
 // device.  Host threads may race to fill an entry; each computes the same
 // value, and the atomic makes the store and the loads well defined.
-static int attention_slots(int d) {
-  static std::atomic<int> cache[2][64];
+template <int D, int NW>
+static int attention_slots() {
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  std::atomic<int>& slot = cache[d == 128 ? 1 : 0][dev];
+  std::atomic<int>& slot = cache[dev];
   int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    hipError_t e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                  &per_cu, attention_kernel<128>, 64 * kAttnWaves, 0)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                  &per_cu, attention_kernel<64>, 64 * kAttnWaves, 0);
+    const hipError_t e =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attention_kernel<D, NW>, 64 * NW, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
     c = max(1, cus * per_cu);
     slot.store(c, std::memory_order_relaxed);
   }
   return c;
+}
+
+// One launch of attention_kernel<D, NW> and, when keys were split, the merge.
+template <int D, int NW>
+static hipError_t run_attention(AttnArgs& A, void* pf_ws, void* dc_ws, hipStream_t s,
+                                hipEvent_t mid) {
+  const ChunkList& chunks = A.chunks;
+  const DecDev& dec = A.dec;
+  const int nq = A.nq, nkv = A.nkv;
+  if (chunks.n > 0 && chunks.n_rows > 0) {
+    const int G = nq / nkv;
+    int max_len = 0;
+    for (int i = 0; i < chunks.n; ++i) max_len = max(max_len, chunks.c[i].len);
+    A.pf_gx = (max_len * G + kPrefillRows - 1) / kPrefillRows;
+    A.pf_ns = 1;
+    A.pf_seg = 1 << 30;
+    // four-wave workgroups run beside many decodes only, where keys are not split
+    if (pf_ws && NW == 2 * kPfHalfWaves) {
+      prefill_split(chunks, nq, nkv, dec.n > 0, &A.pf_ns, &A.pf_seg);
+      if (A.pf_ns <= 1) {
+        A.pf_ns = 1;
+        A.pf_seg = 1 << 30;
+      }
+    }
+    A.pf_wgs = A.pf_gx * A.pf_ns * nkv * chunks.n;
+    A.pf_o = reinterpret_cast<float*>(pf_ws);
+    A.pf_ml = A.pf_ns > 1 ? A.pf_o + (size_t)A.pf_ns * chunks.n_rows * nq * D : nullptr;
+  }
+  if (dec.n > 0) {
+    // decode waves fill the workgroup slots the prefill part leaves free, so
+    // that both kinds run side by side (at least a quarter of the slots)
+    const int slots = attention_slots<D, NW>();
+    const int free_wgs = max(slots - A.pf_wgs, slots / 4);
+    A.dc_slices = max(1, min(free_wgs * NW / nkv, decode_slice_cap(dec.n, nkv, dec.max_ctx)));
+    A.dc_pn = A.dc_slices + dec.n;
+    A.dc_wgs = (A.dc_slices * nkv + NW - 1) / NW;
+    A.dc_o = reinterpret_cast<float*>(dc_ws);
+    A.dc_ml = A.dc_o + (size_t)nq * A.dc_pn * D;
+  }
+  const int wgs = A.pf_wgs + A.dc_wgs;
+  if (wgs == 0) return mid ? hipEventRecord(mid, s) : hipSuccess;
+  // chunk rows need the merge only when their keys were split; decode rows
+  // whenever there is more than one slice
+  A.merge_row0 = A.pf_ns > 1 ? 0 : chunks.n_rows;
+  const int merge_rows = chunks.n_rows + dec.n - A.merge_row0;
+  const bool merge = (A.pf_ns > 1 || A.dc_slices > 1) && merge_rows > 0;
+  hipLaunchKernelGGL((attention_kernel<D, NW>), dim3(wgs), dim3(64 * NW), 0, s, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
+  if (!merge) return hipSuccess;
+  hipLaunchKernelGGL(attention_merge_kernel<D>, dim3(nq, merge_rows), dim3(64), 0, s, A);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const ChunkList& chunks,
@@ -564,58 +682,23 @@ hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const Chunk
   A.nq = nq;
   A.nkv = nkv;
   A.chunks = chunks;
-  const int G = nq / nkv;
-  if (chunks.n > 0 && chunks.n_rows > 0) {
-    int max_len = 0;
-    for (int i = 0; i < chunks.n; ++i) max_len = max(max_len, chunks.c[i].len);
-    A.pf_gx = (max_len * G + kPrefillRows - 1) / kPrefillRows;
-    A.pf_ns = 1;
-    A.pf_seg = 1 << 30;
-    if (pf_ws) {
-      prefill_split(chunks, nq, nkv, dec.n > 0, &A.pf_ns, &A.pf_seg);
-      if (A.pf_ns <= 1) {
-        A.pf_ns = 1;
-        A.pf_seg = 1 << 30;
-      }
-    }
-    A.pf_wgs = A.pf_gx * A.pf_ns * nkv * chunks.n;
-    A.pf_o = reinterpret_cast<float*>(pf_ws);
-    A.pf_ml = A.pf_ns > 1 ? A.pf_o + (size_t)A.pf_ns * chunks.n_rows * nq * d : nullptr;
-  }
   A.dec = dec;
   A.dc_row0 = dec_row0;
-  if (dec.n > 0) {
-    // decode waves fill the workgroup slots the prefill part leaves free, so
-    // that both kinds run side by side (at least a quarter of the slots)
-    const int slots = attention_slots(d);
-    const int free_wgs = max(slots - A.pf_wgs, slots / 4);
-    A.dc_slices =
-        max(1, min(free_wgs * kAttnWaves / nkv, decode_slice_cap(dec.n, nkv, dec.max_ctx)));
-    A.dc_pn = A.dc_slices + dec.n;
-    A.dc_wgs = (A.dc_slices * nkv + kAttnWaves - 1) / kAttnWaves;
-    A.dc_o = reinterpret_cast<float*>(dc_ws);
-    A.dc_ml = A.dc_o + (size_t)nq * A.dc_pn * d;
-  }
-  const int wgs = A.pf_wgs + A.dc_wgs;
-  if (wgs == 0) return mid ? hipEventRecord(mid, s) : hipSuccess;
-  // chunk rows need the merge only when their keys were split; decode rows
-  // whenever there is more than one slice
-  A.merge_row0 = A.pf_ns > 1 ? 0 : chunks.n_rows;
-  const int merge_rows = chunks.n_rows + dec.n - A.merge_row0;
-  const bool merge = (A.pf_ns > 1 || A.dc_slices > 1) && merge_rows > 0;
+  // Eight-wave workgroups split each chunk row group's keys between two wave
+  // groups.  Beside decodes, a chunk whose row groups alone fill half of the
+  // four-wave workgroup slots keeps four-wave workgroups instead: every CU
+  // then holds a prefill and a decode workgroup (MFMA-bound and HBM-bound
+  // waves side by side), where eight-wave prefill workgroups would take
+  // every slot and leave the decodes waiting.
+  int base = 0;
+  for (int i = 0; i < chunks.n; ++i)
+    base += (chunks.c[i].len * (nq / nkv) + kPrefillRows - 1) / kPrefillRows * nkv;
+  const bool four = dec.n > 0 && base >= kPfFourWaveFrom;
   if (d == 128)
-    hipLaunchKernelGGL(attention_kernel<128>, dim3(wgs), dim3(64 * kAttnWaves), 0, s, A);
-  else
-    hipLaunchKernelGGL(attention_kernel<64>, dim3(wgs), dim3(64 * kAttnWaves), 0, s, A);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (mid && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
-  if (!merge) return hipSuccess;
-  if (d == 128)
-    hipLaunchKernelGGL(attention_merge_kernel<128>, dim3(nq, merge_rows), dim3(64), 0, s, A);
-  else
-    hipLaunchKernelGGL(attention_merge_kernel<64>, dim3(nq, merge_rows), dim3(64), 0, s, A);
-  return hipGetLastError();
+    return four ? run_attention<128, 4>(A, pf_ws, dc_ws, s, mid)
+                : run_attention<128, 8>(A, pf_ws, dc_ws, s, mid);
+  return four ? run_attention<64, 4>(A, pf_ws, dc_ws, s, mid)
+              : run_attention<64, 8>(A, pf_ws, dc_ws, s, mid);
 }
 
 hipError_t launch_prefill_attention(const bf16* qkv, int nq, int nkv, int d,
