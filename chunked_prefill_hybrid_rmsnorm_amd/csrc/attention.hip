@@ -158,7 +158,8 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   static_assert(NW == kPfHalfWaves || NW == 2 * kPfHalfWaves, "one or two wave groups");
   constexpr int NGROUPS = NW / kPfHalfWaves;
   const int l16 = lane & 15, q = lane >> 4;
-  const int half = wave_id / kPfHalfWaves, wave = wave_id % kPfHalfWaves;
+  const int half = NGROUPS == 1 ? 0 : wave_id / kPfHalfWaves;  // the wave's group
+  const int wave = wave_id % kPfHalfWaves;
   char* ring = ring_all + half * kPfStages * PfStage<D>::BYTES;
   const int per_chunk = A.pf_gx * A.pf_ns * A.nkv;
   const int c = b / per_chunk;
@@ -231,7 +232,11 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   static_assert(kPfStages == 3, "the waits below count one step in flight behind the current");
   if (my_n > 0) issue(0);
   if (my_n > 1) issue(1);
-  for (int i = 0; i < n_iter; ++i) {
+  // the group's own steps (the same loop shape as a single group, so that
+  // `busy`, invariant, can take the whole loop apart), then a barrier for
+  // each step the other group has beyond them (at most one)
+  int i = 0;
+  for (; i < my_n; ++i) {
     // this step's copies have landed (the next step's may still be in flight)
     if (i + 1 < my_n)
       wait_vmcnt<PfStage<D>::PER_WAVE>();
@@ -241,12 +246,13 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (i + 2 < my_n) issue(i + 2);
-    if (!busy || i >= my_n) continue;
+    if (!busy) continue;
     KvFrag<D> f;
     prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
     const int t0 = kg0 + i * 32;
     compute_step<D, 2>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale, q);
   }
+  for (; i < n_iter; ++i) __builtin_amdgcn_s_barrier();
   // group 1 hands its rows' (m, l, o) to group 0 through the rings' LDS:
   // per wave and row block, D/4 + 2 floats per lane, lane-minor
   constexpr int XF = D / 4 + 2;
