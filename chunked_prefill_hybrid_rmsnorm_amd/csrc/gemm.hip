@@ -174,6 +174,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_norm(
 struct Choice {
   int big;     // 1: 288-row tile, 0: 128-row tile
   int bn96;    // 1: 96-column tile (288-row tiles of plain / residual GEMMs)
+  int bn64;    // 1: 64-column tile (288-row tiles of residual GEMMs)
   int splits;  // K splits (1 = none)
 };
 
@@ -190,6 +191,7 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   Choice c;
   c.big = mp > 128 ? 1 : 0;
   c.bn96 = 0;
+  c.bn64 = 0;
   const int bm = c.big ? 288 : 128;
   const int mt = (mp + bm - 1) / bm;
   const int ksteps = k / kGemmBK;
@@ -201,6 +203,18 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   }
   const int t128 = mt * ((n + 127) / 128);
   c.splits = splits_for(t128, ksteps);
+  // residual GEMMs with short k loops (the O projection): 64-column tiles
+  // need half the K splits, so half the fp32 partials to write and reduce,
+  // which outweighs re-reading A for twice as many column tiles
+  if (c.big && epi == EPI_RESIDUAL && ksteps <= 64) {
+    const int t64 = mt * ((n + 63) / 64);
+    const int s64 = splits_for(t64, ksteps);
+    if (t64 * s64 <= 256 && t64 * s64 >= t128 * c.splits) {
+      c.bn64 = 1;
+      c.splits = s64;
+      return c;
+    }
+  }
   if (c.big && ksteps >= 32) {
     // narrower tiles when they fill more CUs (QKV-like widths); they sum K in
     // two k-groups, so short-K shapes keep the 128-column tile and with it the
@@ -227,6 +241,10 @@ template <int EPI>
 static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2,
                              bf16* c, const bf16* r, float* part, int m, int mp, int n, int k,
                              hipStream_t s) {
+  if constexpr (EPI == EPI_RESIDUAL) {
+    if (ch.big && ch.bn64)
+      return run_gemm_dma<288, 64, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  }
   if constexpr (EPI != EPI_SWIGLU) {
     if (ch.big && ch.bn96)
       return run_gemm_dma<288, 96, 2, 2, EPI, 3, 64, 2>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
