@@ -333,6 +333,19 @@ def test_prefill_attention_without_split_long_prefix():
     assert_close("attn (layer)", gpu["attn"], ref.taps["attn"])
 
 
+def test_layer_head_dim64_four_wave_attention():
+    """Head dim 64 with a chunk of 256 row groups (1024 rows x 32 kv heads)
+    beside decodes: the attention runs four-wave workgroups (no key split
+    inside a workgroup), the path the Llama-70B-shaped batch takes at d = 128."""
+    from chunked_prefill_hybrid_rmsnorm_amd.inputs import LayerShape
+    _flush("head dim 64, 1024-row chunk x 32 kv heads + 3 decodes (four-wave attention)")
+    shape = LayerShape(2048, 32, 32, 64, 1024)
+    hb = make_hybrid_batch(shape, chunk_lens=[1024], chunk_starts=[0], n_decodes=3,
+                           ctx_range=(30, 200), seed=31, random_gains=True)
+    _, gpu = run_gpu(hb)
+    check_layer(hb, gpu, run_oracle(hb))
+
+
 def test_layer_llama70_full_size():
     _flush("llama2-70b-shaped: Lp=512 after 3584 cached + 64 decodes ctx U[512,4096]")
     from chunked_prefill_hybrid_rmsnorm_amd.inputs import llama70_batch
