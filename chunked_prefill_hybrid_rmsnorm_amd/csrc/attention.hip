@@ -57,7 +57,7 @@ struct AttnArgs {
   int dc_row0;   // first decode row
   int dc_slices;  // slices per kv head the grid provides (upper bound of P)
   int dc_pn;      // partial slots per q head = dc_slices + n
-  int dc_wgs;     // decode workgroups = ceil(dc_slices * nkv / 4)
+  int dc_wgs;     // decode workgroups = ceil(dc_slices * nkv / waves per workgroup)
   float* dc_o;
   float* dc_ml;
   int merge_row0;  // first row the merge grid covers (chunk rows only when keys were split)
@@ -148,10 +148,11 @@ __device__ __forceinline__ void merge_acc(AttnAcc<D>& a, float m1, float l1, con
 // one kv head, 32 per wave as two 16-row MFMA blocks, over one key segment.
 // With eight waves (NW = 8) they form two groups of four on the same rows:
 // group 0 takes the first half of the segment's 32-key steps, group 1 the
-// rest, so every SIMD holds two waves of the workgroup.  Each group copies its steps' K/V pages into its own LDS
-// ring (global -> LDS, kPfStages deep) and reads them from there, so a K/V
-// byte crosses the L2 -> CU path once per 128 rows.  At the end group 1 hands
-// its (m, l, o) to group 0 through LDS, which merges and stores the rows.
+// rest, so every SIMD holds two waves of the workgroup.  Each group copies
+// its steps' K/V pages into its own LDS ring (global -> LDS, kPfStages deep)
+// and reads them from there, so a K/V byte crosses the L2 -> CU path once per
+// 128 rows.  At the end group 1 hands its (m, l, o) to group 0 through LDS,
+// which merges and stores the rows.
 template <int D, int NW>
 __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave_id, int lane,
                                               char* ring_all) {
