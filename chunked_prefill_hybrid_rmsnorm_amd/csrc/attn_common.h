@@ -120,15 +120,14 @@ __device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<
   for (int rb = 0; rb < NRB; ++rb) {
     AttnAcc<D>& acc = a[rb];
     const bool full = t0 + 31 <= min(lim_min[rb], k_end - 1);  // wave-uniform
+    // the scale (> 0) is applied once to the row maximum and inside the
+    // exponent's fma below, not to every score
     float smax = -INFINITY;
     if (full) {
 #pragma unroll
       for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[rb][hp][r] *= scale;
-          smax = fmaxf(smax, s[rb][hp][r]);
-        }
+        for (int r = 0; r < 4; ++r) smax = fmaxf(smax, s[rb][hp][r]);
     } else {
       const int lim = min(row_limit[rb], k_end - 1);
 #pragma unroll
@@ -136,11 +135,11 @@ __device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + 8 * q + 4 * hp + r;
-          s[rb][hp][r] = t <= lim ? s[rb][hp][r] * scale : -INFINITY;
+          s[rb][hp][r] = t <= lim ? s[rb][hp][r] : -INFINITY;
           smax = fmaxf(smax, s[rb][hp][r]);
         }
     }
-    smax = quad_max(smax);
+    smax = quad_max(smax) * scale;
     // move the max in use only when the new one is well above it; a row with
     // no visible key so far keeps m = -inf and uses 0 as its shift, so that
     // no -inf - -inf appears (its probabilities are exactly 0)
@@ -161,7 +160,7 @@ __device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(s[rb][hp][r] - m_use);
+        p[r] = fast_exp2(__builtin_fmaf(s[rb][hp][r], scale, -m_use));
         psum += p[r];
       }
       pk[hp * 2 + 0] = pack2(p[0], p[1]);
