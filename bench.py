@@ -184,6 +184,24 @@ def main():
         graph = {"ms_per_step": round(gms, 5), "value": round(M / (gms / 1e3), 1)}
         log(f"layer (graph replay) {gms * 1e3:.1f} us/step, {M / (gms / 1e3) / 1e6:.3f} M tokens/s")
 
+    # spread of single calls: one event between consecutive calls (each
+    # interval holds one call plus one event record)
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    for i in range(a.warmup):
+        layer(i)
+    bounds[0].record()
+    for i in range(a.steps):
+        layer(i)
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    per_call = sorted(bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(a.steps))
+
+    def pct(q):
+        return round(per_call[min(len(per_call) - 1, int(q * len(per_call)))], 2)
+
+    spread = {"p10_us": pct(0.1), "p50_us": pct(0.5), "p90_us": pct(0.9)}
+    log(f"per call: p10 {spread['p10_us']} us, p50 {spread['p50_us']} us, p90 {spread['p90_us']} us")
+
     # per-step times inside the real layer sequence: HIP events recorded by the
     # library between its steps, on the stream it launches on
     log("per-step timing with stage events ...")
@@ -257,6 +275,7 @@ def main():
                            "frac": round(t_roof / (ms * 1e-3), 4)},
         "stages": table,
         "graph_replay": graph,
+        "per_call": spread,
     }
     if not a.no_cpu_baseline:
         log("timing the CPU oracle ...")
