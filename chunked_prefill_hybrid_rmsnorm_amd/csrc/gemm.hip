@@ -205,10 +205,11 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   c.splits = splits_for(t128, ksteps);
   // residual GEMMs with short k loops (the O projection): 64-column tiles
   // need half the K splits, so half the fp32 partials to write and reduce,
-  // which outweighs re-reading A for twice as many column tiles.  They sum K
-  // in two k-groups, so very short k loops (< 32 steps) keep the 128-column
+  // which outweighs re-reading A for twice as many column tiles (and where
+  // the 128-column tile gives few workgroups, doubles them).  They sum K in
+  // two k-groups, so very short k loops (< 16 steps) keep the 128-column
   // tile and its per-element summation order, that of the 128-row tile.
-  if (c.big && epi == EPI_RESIDUAL && ksteps >= 32 && ksteps <= 64) {
+  if (c.big && epi == EPI_RESIDUAL && ksteps >= 16 && ksteps <= 64) {
     const int t64 = mt * ((n + 63) / 64);
     const int s64 = splits_for(t64, ksteps);
     if (t64 * s64 <= 256 && t64 * s64 >= t128 * c.splits) {
