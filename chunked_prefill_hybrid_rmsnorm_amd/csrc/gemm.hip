@@ -262,6 +262,14 @@ static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, con
       return run_gemm_dma<288, 128, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
     return run_gemm_dma<288, 128, 2, 4, EPI, 3, 64, 1, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
   }
+  // small batches (decode-heavy iterations): the row tile shrinks with the
+  // batch, so each k-step copies fewer (clamped, repeated) activation rows
+  // beside the same weight rows; the per-element summation order is that of
+  // the 128-row tile
+  if (mp <= 32)
+    return run_gemm_dma<32, 128, 1, 4, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  if (mp <= 64)
+    return run_gemm_dma<64, 128, 2, 2, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
   return run_gemm_dma<128, 128, 2, 2, EPI, 4>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
 }
 
