@@ -77,7 +77,10 @@ def test_rmsnorm_step():
                                             # with two splits of 8 k-steps; ragged last
                                             # column tile
                                             (200, 208, 320, 64, False),
-                                            (150, 160, 320, 1024, True)])
+                                            (150, 160, 320, 1024, True),
+                                            # small-batch row tiles (64 and 32 rows)
+                                            (40, 48, 384, 1024, True),
+                                            (25, 32, 256, 2048, False)])
 def test_gemm_step(m, mp, n, k, split):
     """Without a workspace K is not split (one launch, the long-k tile with two
     k-groups for the 288-row shapes); with one the partials are reduced."""
@@ -105,7 +108,8 @@ def test_gemm_step(m, mp, n, k, split):
     assert_close("gemm+residual", tap_f64(c2, m), ref[:m] + widen(r))
 
 
-@pytest.mark.parametrize("mp,f,k", [(96, 1024, 512), (272, 1024, 4096)])
+@pytest.mark.parametrize("mp,f,k", [(32, 1024, 512), (64, 1024, 512), (96, 1024, 512),
+                                    (272, 1024, 4096)])
 def test_swiglu_step(mp, f, k):
     import torch
     rng = np.random.default_rng(5)
