@@ -175,6 +175,7 @@ struct Choice {
   int big;     // 1: 288-row tile, 0: 128-row tile
   int bn96;    // 1: 96-column tile (288-row tiles of plain / residual GEMMs)
   int bn64;    // 1: 64-column tile (288-row tiles of residual GEMMs)
+  int r256;    // 1: 256-row tiles instead of 288 (fewer padded rows)
   int splits;  // K splits (1 = none)
 };
 
@@ -192,7 +193,10 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   c.big = mp > 128 ? 1 : 0;
   c.bn96 = 0;
   c.bn64 = 0;
-  const int bm = c.big ? 288 : 128;
+  // past one 288-row tile, 256-row tiles when they pad fewer rows (512 rows:
+  // two of 256 instead of two of 288)
+  c.r256 = mp > 288 && (mp + 255) / 256 * 256 < (mp + 287) / 288 * 288 ? 1 : 0;
+  const int bm = c.big ? (c.r256 ? 256 : 288) : 128;
   const int mt = (mp + bm - 1) / bm;
   const int ksteps = k / kGemmBK;
   if (epi == EPI_SWIGLU) {
@@ -240,28 +244,34 @@ size_t gemm_workspace_bytes(GemmEpilogue epi, int mp, int n, int k) {
   return c.splits > 1 ? (size_t)c.splits * mp * width * sizeof(float) : 0;
 }
 
+// Row tile BM (288 or 256) of the large-batch GEMMs.
+template <int EPI, int BM>
+static hipError_t run_big(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
+                          const bf16* r, float* part, int m, int mp, int n, int k, hipStream_t s) {
+  if constexpr (EPI == EPI_RESIDUAL) {
+    if (ch.bn64)
+      return run_gemm_dma<BM, 64, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  }
+  if constexpr (EPI != EPI_SWIGLU) {
+    if (ch.bn96)
+      return run_gemm_dma<BM, 96, 2, 2, EPI, 3, 64, 2>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  }
+  // the 128-column tiles run the two waves of a SIMD half a k-step apart
+  // (ping-pong); the 96-column tile, whose k loops are short, does not gain
+  // from it.
+  // long k loops amortise the k-group reduction: 4 waves per group, each
+  // with a (BM / 2) x 64 sub-tile (fewer LDS bytes per MFMA)
+  if ((k / kGemmBK) / ch.splits >= 48)
+    return run_gemm_dma<BM, 128, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+  return run_gemm_dma<BM, 128, 2, 4, EPI, 3, 64, 1, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
+}
+
 template <int EPI>
 static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2,
                              bf16* c, const bf16* r, float* part, int m, int mp, int n, int k,
                              hipStream_t s) {
-  if constexpr (EPI == EPI_RESIDUAL) {
-    if (ch.big && ch.bn64)
-      return run_gemm_dma<288, 64, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
-  }
-  if constexpr (EPI != EPI_SWIGLU) {
-    if (ch.big && ch.bn96)
-      return run_gemm_dma<288, 96, 2, 2, EPI, 3, 64, 2>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
-  }
-  if (ch.big) {
-    // the 128-column tiles run the two waves of a SIMD half a k-step apart
-    // (ping-pong); the 96-column tile, whose k loops are short, does not gain
-    // from it.
-    // long k loops amortise the k-group reduction: 4 waves per group, each
-    // with a 144 x 64 sub-tile (fewer LDS bytes per MFMA)
-    if ((k / kGemmBK) / ch.splits >= 48)
-      return run_gemm_dma<288, 128, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
-    return run_gemm_dma<288, 128, 2, 4, EPI, 3, 64, 1, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
-  }
+  if (ch.big && ch.r256) return run_big<EPI, 256>(ch, a, w, w2, c, r, part, m, mp, n, k, s);
+  if (ch.big) return run_big<EPI, 288>(ch, a, w, w2, c, r, part, m, mp, n, k, s);
   // small batches (decode-heavy iterations): the row tile shrinks with the
   // batch, so each k-step copies fewer (clamped, repeated) activation rows
   // beside the same weight rows; the per-element summation order is that of

@@ -80,7 +80,9 @@ def test_rmsnorm_step():
                                             (150, 160, 320, 1024, True),
                                             # small-batch row tiles (64 and 32 rows)
                                             (40, 48, 384, 1024, True),
-                                            (25, 32, 256, 2048, False)])
+                                            (25, 32, 256, 2048, False),
+                                            # two 256-row tiles (fewer padded rows than 288)
+                                            (500, 512, 384, 1024, True)])
 def test_gemm_step(m, mp, n, k, split):
     """Without a workspace K is not split (one launch, the long-k tile with two
     k-groups for the 288-row shapes); with one the partials are reduced."""
