@@ -193,9 +193,9 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   c.big = mp > 128 ? 1 : 0;
   c.bn96 = 0;
   c.bn64 = 0;
-  // past one 288-row tile, 256-row tiles when they pad fewer rows (512 rows:
-  // two of 256 instead of two of 288)
-  c.r256 = mp > 288 && (mp + 255) / 256 * 256 < (mp + 287) / 288 * 288 ? 1 : 0;
+  // large batches: 256-row tiles whenever they pad fewer rows than 288-row
+  // ones (129-256 rows, 512 rows as two of 256, ...)
+  c.r256 = mp > 128 && (mp + 255) / 256 * 256 < (mp + 287) / 288 * 288 ? 1 : 0;
   const int bm = c.big ? (c.r256 ? 256 : 288) : 128;
   const int mt = (mp + bm - 1) / bm;
   const int ksteps = k / kGemmBK;
