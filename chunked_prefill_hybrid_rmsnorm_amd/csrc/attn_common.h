@@ -72,10 +72,14 @@ __device__ __forceinline__ void load_step(KvFrag<D>& f, const KvDev& kv, int g, 
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) f.k[hp][ks] = ld16(kp + ks * 32);
   }
+  // V: every instruction reads whole lines (512 contiguous bytes per page)
+  // that nothing reads again, so the loads are non-temporal.  K stays
+  // ordinary: each of its lines is read in two halves by consecutive loads.
   const int pv = q < 2 ? p0 : p1;
   const bf16* vp = kv.v_page(max(pv, 0), g) + (q & 1) * 8 + l16 * 16;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) f.v[db] = ld16(vp + db * 256);
+  for (int db = 0; db < D / 16; ++db)
+    f.v[db] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + db * 256));
 }
 
 // Largest growth of the running max (base-2 units) that is not folded into
