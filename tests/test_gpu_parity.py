@@ -370,3 +370,29 @@ def test_layer_tensor_parallel_share_full_size(which):
     _, gpu = run_gpu(hb)
     check_layer(hb, gpu, run_oracle(hb))
 
+
+
+def _random_batch_args(seed):
+    """Seeded draw of one batch layout: 0-3 chunks with ragged lengths and
+    starts, 0-40 decodes with contexts up to 900 tokens, one of the small
+    shapes and a padding granularity; at least one row."""
+    rng = np.random.default_rng(1000 + seed)
+    shape = (TINY, D128, G8)[seed % 3]
+    n_chunks = int(rng.integers(0, 4))
+    chunk_lens = [int(v) for v in rng.integers(1, 201, size=n_chunks)]
+    chunk_starts = [int(v) for v in rng.integers(0, 601, size=n_chunks)]
+    n_dec = int(rng.integers(0 if n_chunks else 1, 41))
+    ctx_lens = [int(v) for v in rng.integers(0, 901, size=n_dec)]
+    pad = (16, 32, 128)[int(rng.integers(0, 3))]
+    return shape, dict(chunk_lens=chunk_lens, chunk_starts=chunk_starts, ctx_lens=ctx_lens), pad
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_layer_random_batches(seed):
+    """Seeded random hybrid batches (chunk count, lengths, prefixes, decode
+    contexts, shape and padding all drawn) against the oracle."""
+    shape, args, pad = _random_batch_args(seed)
+    _flush(f"random batch {seed}: {shape} pad={pad} {args}")
+    hb = make_hybrid_batch(shape, seed=seed, random_gains=True, **args)
+    _, gpu = run_gpu(hb, pad=pad)
+    check_layer(hb, gpu, run_oracle(hb))
