@@ -147,12 +147,16 @@ class BatchingLoop:
         import torch
         return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to("cuda", non_blocking=True)
 
-    def run(self, record: bool = False):
+    def run(self, record: bool = False, max_iterations: Optional[int] = None):
+        """Run the loop to the end, or for at most ``max_iterations``
+        iterations.  With ``record`` every iteration's batch and the logits of
+        its sampled rows are kept (one synchronisation per iteration)."""
         import torch
         s, m = self.m.shape, self.m
-        sched = StallFreeScheduler([len(p) for p in self.prompts], self.gen_len, self.budget)
+        sched = StallFreeScheduler([len(p) for p in self.prompts], self.gen_len, self.budget,
+                                   max_chunks=B.HL_MAX_CHUNKS)
         events, records = [], []
-        while True:
+        while max_iterations is None or len(events) < max_iterations:
             b = sched.next_batch()
             if b is None:
                 break

@@ -75,6 +75,24 @@ Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad
   return L;
 }
 
+// Bytes a call with `rows` rows needs.  The split-K partials of the GEMMs are
+// not monotone in the row count (a second row tile halves the splits), so
+// their share is the largest over every padded row count up to this one;
+// every other part grows with rows, decodes and max_ctx.  A workspace sized
+// for max_rows therefore serves every call with fewer rows.
+size_t workspace_need(const hl_config* c, int rows, int n_dec, int max_ctx, int pad) {
+  const Layout L = make_layout(c, rows, n_dec, max_ctx, pad);
+  const int H = c->hidden, F = c->ffn, nqd = c->n_q_heads * c->head_dim;
+  const int nqkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+  size_t g = 0;
+  for (int mp = pad; mp <= L.Mp; mp += pad)
+    g = std::max({g, gemm_workspace_bytes(EPI_STORE, mp, nqkv, H),
+                  gemm_workspace_bytes(EPI_RESIDUAL, mp, H, nqd),
+                  gemm_workspace_bytes(EPI_RESIDUAL, mp, H, F),
+                  gemm_workspace_bytes(EPI_SWIGLU, mp, F, H)});
+  return L.gemm + align256(g);
+}
+
 int fill_chunks(const hl_chunk* chunks, int n_chunks, ChunkList* cl) {
   if (n_chunks < 0) return HL_ERR_SHAPE;
   if (n_chunks > HL_MAX_CHUNKS) return HL_ERR_UNSUPPORTED;
@@ -130,7 +148,7 @@ int hl_workspace_bytes(const hl_config* cfg, int32_t max_rows, int32_t max_decod
   if (e) return e;
   if (!bytes) return HL_ERR_NULL;
   if (max_rows < 0 || max_decodes < 0 || max_ctx < 0 || pad <= 0 || pad % 16) return HL_ERR_SHAPE;
-  *bytes = make_layout(cfg, max_rows, max_decodes, max_ctx, pad).total;
+  *bytes = workspace_need(cfg, max_rows, max_decodes, max_ctx, pad);
   return HL_OK;
 }
 
@@ -173,7 +191,7 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
   const int M = cl.n_rows + dd.n;
   if (M == 0) return HL_ERR_SHAPE;
   const Layout L = make_layout(cfg, M, dd.n, dd.max_ctx, pad);
-  if (ws_bytes < L.total) return HL_ERR_WORKSPACE;
+  if (ws_bytes < workspace_need(cfg, M, dd.n, dd.max_ctx, pad)) return HL_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return HL_ERR_WORKSPACE;
 
   char* base = static_cast<char*>(ws);
@@ -447,6 +465,7 @@ int hl_decode_attention(const hl_config* cfg, const hl_bf16* qkv, int32_t row0,
   if (row0 < 0) return HL_ERR_SHAPE;
   if (dd.n == 0) return HL_OK;
   if (!ws) return HL_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return HL_ERR_WORKSPACE;  // f32x4 partial stores
   if (ws_bytes <
       decode_workspace_bytes(dd.n, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, dd.max_ctx))
     return HL_ERR_WORKSPACE;

@@ -29,7 +29,7 @@ __device__ __forceinline__ void lds_copy16(const bf16* base, uint32_t voff, char
   const uint32_t dst = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
                "s"(base), "s"(dst)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Instruction schedule of one stage's fragment reads and MFMAs: kLead LDS

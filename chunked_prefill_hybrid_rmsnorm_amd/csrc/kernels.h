@@ -1,4 +1,4 @@
-// Internal launchers shared by the C-ABI layer (api.cpp) and the kernels.
+// Internal launchers shared by the C-ABI layer (api.hip) and the kernels.
 #pragma once
 #include "common.h"
 

@@ -193,8 +193,10 @@ __global__ __launch_bounds__(256) void rope_kv_append_kernel(
   } else {
     row_pos_slot(chunks, dec, kv.page_size, kv.num_pages, r, &pos, &slot);
   }
-  const int page = slot >= 0 ? slot / kv.page_size : -1;
-  const int off = slot >= 0 ? slot % kv.page_size : 0;
+  // a slot outside the pool (negative, or a page id >= num_pages) writes no KV
+  const bool in_pool = slot >= 0 && slot / kv.page_size < kv.num_pages;
+  const int page = in_pool ? slot / kv.page_size : -1;
+  const int off = in_pool ? slot % kv.page_size : 0;
   __shared__ float cs_tab[64], sn_tab[64];  // d/2 <= 64
   if (threadIdx.x < half)
     rope_cos_sin(pos, freq.inv[threadIdx.x], &cs_tab[threadIdx.x], &sn_tab[threadIdx.x]);

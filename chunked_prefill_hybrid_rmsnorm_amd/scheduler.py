@@ -9,7 +9,8 @@ iteration forms one hybrid batch of at most ``budget`` rows --
    ``min(prompt left, budget left)`` tokens (with new requests admitted only
    while budget is left, at most one prompt is ever partly prefilled);
 3. new requests in arrival order while budget is left, each with a chunk of
-   ``min(prompt, budget left)`` tokens.
+   ``min(prompt, budget left)`` tokens, up to ``max_chunks`` chunks in the
+   batch (the layer call's limit, HL_MAX_CHUNKS).
 
 A chunk that completes its prompt yields the request's first generated token
 from its last row; every decode row yields the next one.  A request leaves
@@ -68,10 +69,14 @@ class Batch:
 class StallFreeScheduler:
     """Requests all arrive at the start, in ``prompt_lens`` order."""
 
-    def __init__(self, prompt_lens: Sequence[int], gen_len: int, budget: int):
+    def __init__(self, prompt_lens: Sequence[int], gen_len: int, budget: int,
+                 max_chunks: int = 16):
         if budget <= 0 or gen_len <= 0 or any(p <= 0 for p in prompt_lens):
             raise ValueError("budget, gen_len and every prompt length must be positive")
+        if max_chunks <= 0:
+            raise ValueError("max_chunks must be positive")
         self.budget = budget
+        self.max_chunks = max_chunks
         self.reqs = [Request(i, int(p), gen_len) for i, p in enumerate(prompt_lens)]
         self.waiting: List[int] = list(range(len(self.reqs)))
         self.running: List[int] = []   # admitted and not finished, in admission order
@@ -94,7 +99,8 @@ class StallFreeScheduler:
             if c > 0:
                 chunks.append(ChunkWork(r, R[r].prefilled, c))
                 n_t += c
-        while self.waiting and n_t < self.budget:
+        # the layer call takes at most max_chunks chunks per batch
+        while self.waiting and n_t < self.budget and len(chunks) < self.max_chunks:
             r = self.waiting.pop(0)
             self.running.append(r)
             c = min(R[r].prompt_len, self.budget - n_t)

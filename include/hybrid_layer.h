@@ -96,9 +96,12 @@ typedef struct {
 /* Piggybacked decodes, one row each.  Decode j has ctx_lens[j] cached tokens;
  * its new token sits at position ctx_lens[j], is appended there and attends
  * ctx_lens[j] + 1 keys.  block_tables is device int32 [n, max_blocks].
- * max_ctx is a HOST-side upper bound of ctx_lens (sizes the split-K grid
- * without a device read); keys beyond ceil((max_ctx+1)/256)*256 are not
- * visited, so an underestimate gives wrong results, never a fault. */
+ * Row j of block_tables must cover positions [0, ctx_lens[j]] (device
+ * contents are trusted; hl_validate_metadata checks them).  max_ctx is a
+ * HOST-side upper bound of ctx_lens: it sizes the decode workspace and caps
+ * how many key slices the decode attention cuts all decodes' keys into, with
+ * no device read.  Every key of every decode is visited whatever max_ctx
+ * says; an underestimate only makes the slices longer. */
 typedef struct {
   int32_t n;
   const int32_t* ctx_lens;
@@ -131,7 +134,9 @@ const char* hl_error_string(int code);
 
 /* Bytes of workspace hl_layer_forward needs for at most max_rows rows
  * (chunk rows + decodes), max_decodes decodes with contexts up to max_ctx, and
- * row padding `pad` (positive multiple of 16).  Host only. */
+ * row padding `pad` (positive multiple of 16).  Host only.  Nondecreasing in
+ * max_rows, max_decodes and max_ctx: a workspace of this size serves every
+ * call with at most that many rows, decodes and cached tokens. */
 int hl_workspace_bytes(const hl_config* cfg, int32_t max_rows, int32_t max_decodes,
                        int32_t max_ctx, int32_t pad, size_t* bytes);
 
@@ -210,8 +215,9 @@ int hl_gemm_swiglu(const hl_bf16* a, const hl_bf16* w_gate, const hl_bf16* w_up,
 
 /* RoPE on the q and k heads of qkv rows [0, rows) at positions[r] (rotate-half
  * pairing of element i with i + d/2, angle pos * theta^(-2i/d)), written back
- * in place, and append of K (rotated) and V into kv at slots[r] (rows with
- * slot -1 are skipped).  qkv [rows, (nq + 2nkv) d]. */
+ * in place, and append of K (rotated) and V into kv at slots[r].  A row whose
+ * slot is negative or names a page >= kv->num_pages is rotated but writes no
+ * KV.  qkv [rows, (nq + 2nkv) d]. */
 int hl_rope_kv_append(const hl_config* cfg, hl_bf16* qkv, const int32_t* positions,
                       const int32_t* slots, int32_t rows, const hl_kv* kv, hipStream_t stream);
 
@@ -230,7 +236,8 @@ int hl_prefill_workspace_bytes(const hl_config* cfg, const hl_chunk* chunks, int
 /* Paged decode attention.  The 32-key steps of all decodes are cut into equal
  * slices, one per wave, and decodes split over slices are merged afterwards.
  * Decode j reads its q from qkv row row0 + j and writes attn row row0 + j.
- * ws needs hl_decode_workspace_bytes(). */
+ * ws (device, 16-byte aligned, HL_ERR_WORKSPACE otherwise) needs
+ * hl_decode_workspace_bytes(cfg, dec->n, dec->max_ctx). */
 int hl_decode_attention(const hl_config* cfg, const hl_bf16* qkv, int32_t row0,
                         const hl_decodes* dec, const hl_kv* kv, hl_bf16* attn, void* ws,
                         size_t ws_bytes, hipStream_t stream);

@@ -153,3 +153,27 @@ def test_cost_model_slots_are_library_slots(lib):
     from chunked_prefill_hybrid_rmsnorm_amd import roofline as rl
     s = rl.layer_stages(4096, 32, 8, 128, 14336, [256], [768], [1000] * 32)
     assert [x.name for x in s] == B.stage_names() == list(profiling.SLOTS)
+
+
+@pytest.mark.parametrize("shape_name", ["TINY", "MISTRAL_7B", "LLAMA2_70B", "LLAMA2_70B_TP8",
+                                        "MISTRAL_7B_TP4"])
+@pytest.mark.parametrize("pad", [16, 128])
+def test_workspace_bytes_is_nondecreasing(lib, shape_name, pad):
+    """A workspace sized for max_rows serves every call with fewer rows: the
+    size never drops as rows, decodes or contexts grow (the GEMMs' split-K
+    partials alone would drop where a second row tile halves the splits, e.g.
+    288 -> 304 rows of the Mistral-shaped down projection)."""
+    from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
+    cfg = B.make_config(getattr(I, shape_name))
+    prev = 0
+    for rows in range(1, 1200, 3 if pad == 16 else 7):
+        ws = B.hl_workspace_bytes(cfg, rows, 0, 0, pad)
+        assert ws >= prev, (rows, ws, prev)
+        prev = ws
+    top = B.hl_workspace_bytes(cfg, 1200, 64, 4096, pad)
+    for rows, dec, ctx in [(273, 0, 0), (288, 32, 2048), (576, 64, 4096), (1, 1, 1), (1200, 64, 4096)]:
+        assert B.hl_workspace_bytes(cfg, rows, dec, ctx, pad) <= top
+    for dec in range(0, 65, 8):
+        assert B.hl_workspace_bytes(cfg, 600, dec, 4096, pad) <= B.hl_workspace_bytes(cfg, 600, dec + 1, 4096, pad)
+    for ctx in range(0, 5000, 250):
+        assert B.hl_workspace_bytes(cfg, 600, 64, ctx, pad) <= B.hl_workspace_bytes(cfg, 600, 64, ctx + 1, pad)

@@ -100,3 +100,51 @@ def test_loop_matches_oracle_under_teacher_forcing():
         got = greedy(rec.logits)
         for i, (_, rid, k) in enumerate(rec.samples):
             assert toks[rid, k] == got[i], (it, rid, k)
+
+
+def test_loop_mistral_shape_matches_oracle_under_teacher_forcing():
+    """The loop's real shapes: Mistral-7B-shaped layers (4 of the 32), vocabulary
+    32000, 32 requests with prompts U{50..500}, budget 512.  The first two
+    iterations -- many prompt chunks in one batch, then decodes piggybacked on
+    chunks -- replayed by the oracle with the GPU's own tokens."""
+    from chunked_prefill_hybrid_rmsnorm_amd.batching_loop import BatchingLoop, Model, cfg5_prompts
+    from chunked_prefill_hybrid_rmsnorm_amd.inputs import MISTRAL_7B
+    require_gpu()
+    print("mistral-shaped 4-layer model, vocab 32000, 32 requests, budget 512, 2 iterations",
+          flush=True)
+    rng = np.random.default_rng(43)
+    V, L, gen, s = 32000, 4, 100, MISTRAL_7B
+    layers = [draw_weights(rng, s, 0.02, True) for _ in range(L)]
+    table = bf16_bits(rng.standard_normal((V, s.hidden), dtype=np.float32))
+    lm = bf16_bits(rng.standard_normal((V, s.hidden), dtype=np.float32) * np.float32(0.02))
+    gfin = bf16_bits(rng.uniform(0.5, 1.5, s.hidden).astype(np.float32))
+    prompts = cfg5_prompts(32, V, seed=44)
+    model = Model.from_host(s, layers, table, lm, gfin)
+    loop = BatchingLoop(model, prompts, gen, budget=512, seed=45)
+    _, records = loop.run(record=True, max_iterations=2)
+    toks = loop.tokens()
+    assert len(records) == 2
+    assert len(records[0].chunks) > 1, "first batch should hold several prompt chunks"
+    assert records[1].chunks and records[1].decodes, "second batch should be hybrid"
+    print("oracle replay ...", flush=True)
+    ow = [oracle_weights(w) for w in layers]
+    kv = [np.zeros((loop.num_pages, 2, s.n_kv_heads, s.page_size, s.head_dim))
+          for _ in range(L)]
+    tab64, lm64, g64 = widen(table), widen(lm), widen(gfin)
+    for it, rec in enumerate(records):
+        ids = []
+        for rid, start, length in rec.chunks:
+            ids += list(prompts[rid][start:start + length])
+        for rid, ctx in zip(rec.decodes, rec.ctx_lens):
+            ids.append(int(toks[rid, ctx - len(prompts[rid])]))
+        assert len(ids) <= 512
+        chunks = [(length, start, loop.bt[rid][:loop.n_blocks[rid]])
+                  for rid, start, length in rec.chunks]
+        bts = loop.bt[rec.decodes] if rec.decodes else np.zeros((0, loop.max_blocks), np.int32)
+        logits, kv = model_batch(s, ow, tab64, lm64, g64, ids, chunks, rec.ctx_lens, bts, kv)
+        rows = [r for r, _, _ in rec.samples]
+        assert_close(f"iteration {it} logits ({len(ids)} rows, {len(rows)} sampled)",
+                     rec.logits.astype(np.float64), logits[rows])
+        got = greedy(rec.logits)
+        for i, (_, rid, k) in enumerate(rec.samples):
+            assert toks[rid, k] == got[i], (it, rid, k)

@@ -3,12 +3,13 @@
 The library issues only kernel launches on the caller's stream (no memsets,
 no allocations, no host synchronisation), so one layer call can be captured
 and replayed.  Every replay, with ordinary eager work between replays, must
-match the eager call bit for bit: output rows and KV pages."""
+match the eager call bit for bit (output rows and KV pages) and the oracle
+within the parity tolerance."""
 import pytest
 
 from chunked_prefill_hybrid_rmsnorm_amd import binding as B
 from chunked_prefill_hybrid_rmsnorm_amd.inputs import mistral_batch
-from tests.gpu_helpers import require_gpu
+from tests.gpu_helpers import check_layer, require_gpu, run_oracle, tap_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -18,6 +19,7 @@ def test_layer_graph_replays_match_eager():
     require_gpu()
     print("mistral-shaped hybrid batch, seed 1: eager call, capture, 4 replays", flush=True)
     hb = mistral_batch(seed=1)
+    ref = run_oracle(hb)
     db = B.DeviceBatch(hb)
     kv0 = db.kv_t.clone()
     db.forward()  # eager (also settles every one-time host-side query before capture)
@@ -42,3 +44,5 @@ def test_layer_graph_replays_match_eager():
         bits = lambda t: t.view(torch.int16)
         assert torch.equal(bits(db.out), bits(out_ref)), f"replay {rep}: output differs from the eager call"
         assert torch.equal(bits(db.kv_t), bits(kv_ref)), f"replay {rep}: pages differ from the eager call"
+        print(f"replay {rep} against the oracle", flush=True)
+        check_layer(hb, {"out": tap_f64(db.out, db.M), "kv": db.kv_logical()}, ref, taps=False)

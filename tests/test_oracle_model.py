@@ -66,3 +66,32 @@ def test_rows_of_a_batch_are_independent():
                              [k.copy() for k in kv])
     np.testing.assert_allclose(both, np.concatenate([alone_p, alone_d]), rtol=1e-9, atol=1e-9)
     assert greedy(both).shape == (10,)
+
+
+def test_model_batch_equals_dense_torch_stack():
+    """The whole composition against library routines: embedding rows, each
+    layer as a dense torch layer (contiguous K/V, causal SDPA), then
+    F.rms_norm with the final gain and F.linear with the LM head.  Dropping
+    the final norm, its gain or its eps, or transposing the head, fails."""
+    import torch
+    import torch.nn.functional as F
+    from tests.test_oracle_layer import dense_layer_torch
+
+    layers, table, lm, g = _model(5)
+    ids = list(np.random.default_rng(6).integers(0, V, size=19))
+    bt = list(range(pages_for(19, TINY.page_size)))
+    logits, _ = model_batch(TINY, layers, table, lm, g, ids, [(19, 0, bt)], [], [],
+                            _pools(len(bt)))
+    x = table[np.asarray(ids)]
+    for w in layers:
+        x, _, _ = dense_layer_torch(TINY, w, x)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    xn = F.rms_norm(t(x), (TINY.hidden,), t(g), eps=TINY.rms_eps)
+    ref = F.linear(xn, t(lm)).numpy()
+    np.testing.assert_allclose(logits, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+    # the pin is sensitive to the final norm: without it (or its gain) the
+    # logits move far beyond the tolerance above
+    no_norm = F.linear(t(x), t(lm)).numpy()
+    no_gain = F.linear(F.rms_norm(t(x), (TINY.hidden,), eps=TINY.rms_eps), t(lm)).numpy()
+    for wrong in (no_norm, no_gain):
+        assert np.abs(wrong - logits).max() > 1e-3 * np.abs(ref).max()

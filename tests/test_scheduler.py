@@ -99,3 +99,17 @@ def test_bad_arguments():
         StallFreeScheduler([3, 0], 2, 16)
     with pytest.raises(ValueError):
         StallFreeScheduler([3], 2, 0)
+
+
+def test_chunk_count_capped_at_the_layer_limit():
+    """Many short prompts: a batch never holds more chunks than one layer call
+    takes (16), and every prompt is still admitted in arrival order."""
+    from chunked_prefill_hybrid_rmsnorm_amd.binding import HL_MAX_CHUNKS
+    prompts = [3] * 40
+    s, log = run(prompts, 2, 512)
+    assert max(len(b.chunks) for b, _, _ in log) == HL_MAX_CHUNKS
+    order = [c.rid for b, _, _ in log for c in b.chunks if c.start == 0]
+    assert order == list(range(len(prompts)))
+    s2 = StallFreeScheduler(prompts, 2, 512, max_chunks=5)
+    b = s2.next_batch()
+    assert len(b.chunks) == 5 and b.n_rows == 15
