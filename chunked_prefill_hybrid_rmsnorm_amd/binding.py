@@ -21,7 +21,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_
 _lib = None
 
 HL_OK = 0
+HL_ERR_WORKSPACE = -4
 HL_MAX_CHUNKS = 16
+HL_NOALLOC_SCRATCH_BYTES = 160 << 20
 
 
 class HLError(RuntimeError):
@@ -77,6 +79,9 @@ _SIGS = {
                                           _P(hl_chunk), _c.c_int32, _P(hl_decodes), _P(hl_kv),
                                           _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int32,
                                           _P(hl_taps), _P(_c.c_void_p), _c.c_void_p]),
+    "hl_layer_forward_noalloc": (_c.c_int, [_P(hl_config), _P(hl_weights), _c.c_void_p,
+                                            _P(hl_chunk), _c.c_int32, _P(hl_decodes), _P(hl_kv),
+                                            _c.c_void_p, _c.c_int32, _P(hl_taps), _c.c_void_p]),
     "hl_stage_name": (_c.c_char_p, [_c.c_int]),
     "hl_slot_mapping": (_c.c_int, [_P(hl_config), _P(hl_chunk), _c.c_int32, _P(hl_decodes),
                                    _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
@@ -224,6 +229,22 @@ def hl_layer_forward(cfg, weights: hl_weights, x, chunks: Sequence[hl_chunk], de
                                  ws_bytes, pad, ctypes.byref(taps) if taps is not None else None,
                                  _stream(stream))
     _check(rc, "hl_layer_forward")
+
+
+def hl_layer_forward_noalloc(cfg, weights: hl_weights, x, chunks: Sequence[hl_chunk],
+                             dec: hl_decodes, kv: hl_kv, out, pad: int,
+                             taps: Optional[hl_taps] = None, stream=None) -> int:
+    """The layer call on the library's own device workspace; returns the HL
+    code (0, or HL_ERR_WORKSPACE when the batch needs more than the fixed
+    workspace) and raises on any other error."""
+    arr, n = _chunk_array(chunks)
+    rc = load().hl_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x), arr,
+                                         n, ctypes.byref(dec), ctypes.byref(kv), _ptr(out), pad,
+                                         ctypes.byref(taps) if taps is not None else None,
+                                         _stream(stream))
+    if rc not in (HL_OK, HL_ERR_WORKSPACE):
+        _check(rc, "hl_layer_forward_noalloc")
+    return rc
 
 
 N_STAGES = 11

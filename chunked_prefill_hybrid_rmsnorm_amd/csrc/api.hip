@@ -3,11 +3,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "kernels.h"
 
 using namespace hl;
+
+// Workspace of hl_layer_forward_noalloc: a device array of fixed size, one
+// copy per GPU, held from the module's load on that GPU to the end of the
+// process.  Host code never passes its name to a kernel (on the host the name
+// is only a stand-in); it passes the device address looked up per device.
+static __device__ __align__(256) char scratch[HL_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -91,6 +98,30 @@ size_t workspace_need(const hl_config* c, int rows, int n_dec, int max_ctx, int 
                   gemm_workspace_bytes(EPI_RESIDUAL, mp, H, F),
                   gemm_workspace_bytes(EPI_SWIGLU, mp, F, H)});
   return L.gemm + align256(g);
+}
+
+// Device address of `scratch` on the device that runs `stream`, looked up
+// once per device (with that device current) and kept.  Threads that race on
+// the first call store the same address.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HL_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return HL_ERR_HIP;
+    if (sdev != dev) return HL_ERR_UNSUPPORTED;  // the lookup below is per current device
+  }
+  if (dev < 0 || dev >= kMaxDevices) return HL_ERR_UNSUPPORTED;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HL_ERR_HIP;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return HL_OK;
 }
 
 int fill_chunks(const hl_chunk* chunks, int n_chunks, ChunkList* cl) {
@@ -298,6 +329,29 @@ int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_b
     if (!stage_events[i]) return HL_ERR_NULL;
   return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws, ws_bytes, pad, taps,
                             stream, stage_events);
+}
+
+int hl_layer_forward_noalloc(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                             const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                             const hl_kv* kv, hl_bf16* out, int32_t pad, const hl_taps* taps,
+                             hipStream_t stream) {
+  // the size check comes first, so an oversized call fails before any
+  // runtime call (same checks and order as hl_layer_forward otherwise)
+  int e = check_config(cfg);
+  if (e) return e;
+  if (pad <= 0 || pad % 16) return HL_ERR_SHAPE;
+  ChunkList cl;
+  if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
+  DecDev dd;
+  if ((e = fill_decodes(dec, &dd))) return e;
+  const int M = cl.n_rows + dd.n;
+  if (M == 0) return HL_ERR_SHAPE;
+  if (workspace_need(cfg, M, dd.n, dd.max_ctx, pad) > (size_t)HL_NOALLOC_SCRATCH_BYTES)
+    return HL_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((e = scratch_address(stream, &ws))) return e;
+  return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws,
+                            (size_t)HL_NOALLOC_SCRATCH_BYTES, pad, taps, stream, nullptr);
 }
 
 int hl_slot_mapping(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,

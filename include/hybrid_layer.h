@@ -172,6 +172,27 @@ int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_b
                            const hl_taps* taps, hipEvent_t* stage_events, hipStream_t stream);
 const char* hl_stage_name(int stage);
 
+/* hl_layer_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a device array inside
+ * the library, HL_NOALLOC_SCRATCH_BYTES (160 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends; this call allocates
+ * and frees nothing.  Every other argument as for hl_layer_forward.
+ * Errors: HL_ERR_WORKSPACE (nothing enqueued) when the batch needs more than
+ * HL_NOALLOC_SCRATCH_BYTES, i.e. hl_workspace_bytes(cfg, M, dec->n,
+ * dec->max_ctx, pad) > HL_NOALLOC_SCRATCH_BYTES; HL_ERR_UNSUPPORTED when
+ * `stream` belongs to a device other than the current one; HL_ERR_HIP when
+ * the array's device address cannot be looked up.  No part of the array
+ * needs to start at zero: every region is written before it is read within
+ * one call.  All calls on one GPU share the array, so calls that overlap in
+ * time on one GPU (different streams, or threads) race and give wrong
+ * results; calls on one stream run in order and are safe. */
+#define HL_NOALLOC_SCRATCH_BYTES (160u << 20)
+int hl_layer_forward_noalloc(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                             const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                             const hl_kv* kv, hl_bf16* out, int32_t pad, const hl_taps* taps,
+                             hipStream_t stream);
+
 /* Row positions and KV slots of a hybrid batch (PagedAttention addressing:
  * slot = block_table[pos / page_size] * page_size + pos % page_size).
  * positions, slots: device int32 [M], M = sum of chunk lens + dec->n.  A row

@@ -177,3 +177,32 @@ def test_workspace_bytes_is_nondecreasing(lib, shape_name, pad):
         assert B.hl_workspace_bytes(cfg, 600, dec, 4096, pad) <= B.hl_workspace_bytes(cfg, 600, dec + 1, 4096, pad)
     for ctx in range(0, 5000, 250):
         assert B.hl_workspace_bytes(cfg, 600, 64, ctx, pad) <= B.hl_workspace_bytes(cfg, 600, 64, ctx + 1, pad)
+
+
+def test_noalloc_limit_matches_header(lib):
+    """The fixed device workspace of hl_layer_forward_noalloc: the header's
+    size is the binding's, and the Mistral- and Llama-2-70B-shaped batches fit
+    it while a far larger batch does not (checked on the host sizes only)."""
+    from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+HL_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.HL_NOALLOC_SCRATCH_BYTES
+    lim = B.HL_NOALLOC_SCRATCH_BYTES
+    assert B.hl_workspace_bytes(B.make_config(I.MISTRAL_7B), 288, 32, 2048, 16) <= lim
+    assert B.hl_workspace_bytes(B.make_config(I.LLAMA2_70B), 576, 64, 4096, 16) <= lim
+    assert B.hl_workspace_bytes(B.make_config(I.LLAMA2_70B), 4096, 64, 4096, 16) > lim
+
+
+def test_noalloc_rejects_oversized_batch_before_any_runtime_call(lib):
+    """An oversized batch comes back HL_ERR_WORKSPACE from the host checks
+    alone (fake pointers, no GPU touched)."""
+    from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
+    cfg = B.make_config(I.LLAMA2_70B)
+    fake = 0x1000
+    w = B.hl_weights(*([fake] * 7))
+    kv = B.hl_kv(fake, 10)
+    ch = (B.hl_chunk * 1)(B.hl_chunk(4096, 0, fake, 256))
+    dec = B.hl_decodes(0, None, None, 0, 0)
+    assert lib.hl_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w), fake, ch, 1,
+                                        ctypes.byref(dec), ctypes.byref(kv), fake + 4096, 16,
+                                        None, None) == -4
