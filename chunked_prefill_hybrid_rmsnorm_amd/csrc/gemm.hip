@@ -177,6 +177,7 @@ struct Choice {
   int bn64;    // 1: 64-column tile (288-row tiles of residual GEMMs)
   int r256;    // 1: 256-row tiles instead of 288 (fewer padded rows)
   int splits;  // K splits (1 = none)
+  int wide;    // 1: 256-weight-row tile, two stages (two or more row tiles, long k loops)
 };
 
 // Split K (powers of two, at most 8, at least 8 k-steps per split) while the
@@ -199,6 +200,28 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   const int bm = c.big ? (c.r256 ? 256 : 288) : 128;
   const int mt = (mp + bm - 1) / bm;
   const int ksteps = k / kGemmBK;
+  c.wide = 0;
+  if (c.big && mt >= 2 && epi != EPI_STORE) {
+    // two or more row tiles: the MFMA work per weight byte is high enough
+    // that the copies, not the weight stream, bound the k loop; a
+    // 256-weight-row tile (two 64-deep stages fit the LDS) copies fewer
+    // activation bytes per MFMA.  Long k loops only: with fewer than 64
+    // k-steps per split the 128-column tiles were faster (O projection).
+    // Fewer, wider tiles can fill the last round of workgroups worse
+    // (768 rows: 336 wide tiles are 1.3 rounds of 256): keep the wide tile
+    // only where its rounds are at least as full as the default tile's.
+    const int outw = epi == EPI_SWIGLU ? 128 : 256;
+    const int tiles = mt * ((n + outw - 1) / outw);
+    const int sp = splits_for(tiles, ksteps);
+    const int dtiles = mt * ((n + outw / 2 - 1) / (outw / 2));
+    const int dwg = dtiles * splits_for(dtiles, ksteps), wg = tiles * sp;
+    const bool fills = (long long)wg * ((dwg + 255) / 256) >= (long long)dwg * ((wg + 255) / 256);
+    if (wg >= 192 && ksteps / sp >= 64 && fills) {
+      c.wide = 1;
+      c.splits = sp;
+      return c;
+    }
+  }
   if (epi == EPI_SWIGLU) {
     // a tile yields 64 outputs (gate and up rows side by side); narrow FFN
     // shares (tensor-parallel shapes) need K splits to fill the CUs
@@ -248,6 +271,8 @@ size_t gemm_workspace_bytes(GemmEpilogue epi, int mp, int n, int k) {
 template <int EPI, int BM>
 static hipError_t run_big(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
                           const bf16* r, float* part, int m, int mp, int n, int k, hipStream_t s) {
+  if (ch.wide)
+    return run_gemm_dma<BM, 256, 2, 4, EPI, 2, 64, 1>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);
   if constexpr (EPI == EPI_RESIDUAL) {
     if (ch.bn64)
       return run_gemm_dma<BM, 64, 2, 2, EPI, 3, 64, 2, true>(a, w, w2, c, r, part, m, mp, n, k, ch.splits, s);

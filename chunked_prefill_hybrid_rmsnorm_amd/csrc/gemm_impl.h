@@ -91,7 +91,9 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_dma_kernel(
   static_assert(BM % BLK_ROWS == 0 && BN % BLK_ROWS == 0, "tiles are whole copy blocks");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole MFMA blocks");
   static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && (BN / 2) % BLK_ROWS == 0), "swiglu pairing");
-  static_assert(STAGES >= 3, "need at least three stages");
+  // two stages: the copies of step it+1 go into the slot every wave finished
+  // reading before the barrier of step it
+  static_assert(STAGES >= 2, "need at least two stages");
   static_assert(PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
   static_assert(!PP || (STAGES == 3 && NW % 2 == 0 && NBLK % NCW == 0),
                 "ping-pong: three stages, equal copy shares");

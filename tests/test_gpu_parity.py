@@ -82,7 +82,10 @@ def test_rmsnorm_step():
                                             (40, 48, 384, 1024, True),
                                             (25, 32, 256, 2048, False),
                                             # two 256-row tiles (fewer padded rows than 288)
-                                            (500, 512, 384, 1024, True)])
+                                            (500, 512, 384, 1024, True),
+                                            # 256-weight-row tiles with two stages (two row
+                                            # tiles, long k loop): ragged rows, 4 K splits
+                                            (300, 304, 8192, 16384, True)])
 def test_gemm_step(m, mp, n, k, split):
     """Without a workspace K is not split (one launch, the long-k tile with two
     k-groups for the 288-row shapes); with one the partials are reduced."""
@@ -111,7 +114,10 @@ def test_gemm_step(m, mp, n, k, split):
 
 
 @pytest.mark.parametrize("mp,f,k", [(32, 1024, 512), (64, 1024, 512), (96, 1024, 512),
-                                    (272, 1024, 4096)])
+                                    (272, 1024, 4096),
+                                    # 256-weight-row tiles (128 outputs each) over two row
+                                    # tiles; the last column tile is half empty
+                                    (560, 14272, 4096)])
 def test_swiglu_step(mp, f, k):
     import torch
     rng = np.random.default_rng(5)
