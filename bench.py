@@ -1,15 +1,21 @@
 """Throughput of one hybrid-batch decoder-layer forward on one MI355X.
 
-Workload (default): a Mistral-7B-shaped layer (H=4096, 32 q / 8 kv heads,
-head_dim 128, SwiGLU FFN 14336, bf16 weights N(0, 0.02)) over a hybrid batch
-of chunk 4 of a 1024-token prompt (Lp=256, 768 tokens already cached) plus
-Bd=32 decodes with contexts drawn from U{128..2048}; pages of 16 tokens;
-rows padded to 16.  Synthetic, seeded inputs (seed 0).
+Workload (default): a Llama-2-70B-shaped layer (H=8192, 64 q / 8 kv heads,
+head_dim 128, SwiGLU FFN 28672, bf16 weights N(0, 0.01)) over a hybrid batch
+of the last 512-token chunk of a 4096-token prompt (3584 tokens already
+cached) plus Bd=64 decodes with contexts drawn from U{512..4096}; pages of 16
+tokens; rows padded to 16.  This is the largest layer of the workloads that
+fits one GPU unsharded.  Synthetic, seeded inputs (seed 0).  The
+Mistral-7B-shaped layer (Lp=256 after 768 cached + Bd=32 decodes,
+contexts U{128..2048}) is timed briefly beside it (`extra`).
 
 A step is one ``hl_layer_forward`` call (every kernel of the layer).  Inputs
 are resident in HBM before the timed region; R copies of the weights and of
 the KV pool are rotated so that the 256 MB MALL cannot hold one call's
-working set for the next.
+working set for the next.  Before the W warmup steps the layer runs for
+about --settle-ms of GPU time so that the clocks have left their ramp (the
+first ~25 ms of calls run several percent slow); the timed region is exactly
+K steps.
 
 Printed: one JSON line with tokens/s per layer (real rows / time), the
 dominant kernel's roofline figures, the time of every kernel slot of the
@@ -30,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "hybrid-batch tokens/s per layer (Lp+Bd); % peak MFMA (linear), % HBM BW (attn)"
+WORKLOADS = ["llama70", "mistral", "tiny", "llama70_tp8", "mistral_tp4"]
 
 
 def log(msg):
@@ -40,44 +47,55 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    # ~25 ms of layer calls before the timed region: with 10 the GPU's clocks
-    # are still ramping and a step reads ~6 % slower than in steady state
-    p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", choices=["mistral", "llama70", "tiny", "llama70_tp8", "mistral_tp4"],
-                   default="mistral")
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--settle-ms", type=float, default=100.0,
+                   help="GPU time of untimed layer calls before the warmup steps")
+    p.add_argument("--workload", choices=WORKLOADS, default="llama70")
+    p.add_argument("--extra", default="mistral",
+                   help="comma-separated workloads timed briefly beside the main one ('' for none)")
     p.add_argument("--pad", type=int, default=16)
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-runs", type=int, default=2)
+    p.add_argument("--cpu-runs", type=int, default=1)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 256 MiB device-to-device copy first (PMC byte-counter scale)")
     return p.parse_args()
 
 
-def make_batch(name):
+def make_batch(name, seed=0, **kw):
+    """(batch, description, sample builder for the one-thread oracle figure)."""
     from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
     if name == "mistral":
-        return I.mistral_batch(seed=0), (
+        return I.mistral_batch(seed=seed, **kw), (
             "mistral7b-shaped layer: Lp=256 (768 cached) + Bd=32 decodes, ctx U[128,2048]")
     if name == "llama70":
-        return I.llama70_batch(seed=0), (
+        return I.llama70_batch(seed=seed, **kw), (
             "llama2-70b-shaped layer: Lp=512 (3584 cached) + Bd=64 decodes, ctx U[512,4096]")
     if name == "llama70_tp8":
-        return I.llama70_tp8_batch(seed=0), (
+        return I.llama70_tp8_batch(seed=seed, **kw), (
             "llama2-70b layer, one GPU's tensor-parallel share (T=8: 8 q / 1 kv heads, F=3584): "
             "Lp=512 (3584 cached) + Bd=64 decodes, ctx U[512,4096]")
     if name == "mistral_tp4":
-        return I.mistral_tp4_batch(seed=0), (
+        return I.mistral_tp4_batch(seed=seed, **kw), (
             "mistral7b layer, one GPU's tensor-parallel share (T=4: 8 q / 2 kv heads, F=3584): "
             "Lp=256 (768 cached) + Bd=32 decodes, ctx U[128,2048]")
-    return I.tiny_batch(seed=0), "tiny layer H=256: Lp=64 (64 cached) + Bd=4 decodes, ctx U[16,128]"
+    return I.tiny_batch(seed=seed), "tiny layer H=256: Lp=64 (64 cached) + Bd=4 decodes, ctx U[16,128]"
 
 
-def time_loop(fn, steps, warmup):
+def time_loop(fn, steps, warmup, settle_ms=0.0):
     """Average ms per call, HIP events on the current stream (the one the
-    library launches on)."""
+    library launches on).  Untimed: calls for about `settle_ms` of GPU time,
+    then `warmup` calls."""
     import torch
+    if settle_ms > 0:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(0)
+        b.record()
+        torch.cuda.synchronize()
+        for i in range(int(settle_ms / max(a.elapsed_time(b), 1e-3))):
+            fn(i)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -93,15 +111,30 @@ def time_loop(fn, steps, warmup):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def cpu_baseline(hb, runs):
-    """The oracle as it stands, on the same workload, on the host cores."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(hb, name, runs):
+    """The oracle as it stands, on the host cores: `runs` full calls of the
+    benchmarked batch with every BLAS thread, and one call of a bounded
+    sample of the same layer (16 chunk rows at the end of the same cached
+    prefix plus 4 decodes, same weights) on one thread."""
     import numpy as np
+    from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
     from oracle import layer_forward
     from tests.oracle_inputs import oracle_args
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     args = oracle_args(hb)
     times = []
@@ -110,38 +143,45 @@ def cpu_baseline(hb, runs):
         layer_forward(*args)
         times.append(time.perf_counter() - t)
     t_med = sorted(times)[len(times) // 2]
-    return {"value": hb.x.shape[0] / t_med, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{runs} full calls of the benchmarked hybrid batch "
-                      f"(M={hb.x.shape[0]} rows), float64 numpy oracle, median "
-                      f"{t_med:.2f} s/call; host os.cpu_count()={os.cpu_count()}"}
+    M = hb.x.shape[0]
+    res = {"value": round(M / t_med, 2), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{runs} full call(s) of the benchmarked hybrid batch (M={M} rows), float64 "
+                     f"numpy oracle with {threads} BLAS threads, median {t_med:.2f} s/call",
+           "cpu_model": _cpu_model(), "host_cpu_count": os.cpu_count(),
+           "run_seconds": [round(t, 3) for t in times]}
+    # one thread, on a bounded sample of the same layer (same weights and
+    # cached-prefix length, fewer rows)
+    c0 = hb.chunks[0] if hb.chunks else None
+    ctx = hb.decodes.ctx_lens
+    lo, hi = (int(ctx.min()), int(ctx.max())) if len(ctx) else (16, 128)
+    n_rows = min(16, c0.length) if c0 else 0
+    sample = I.make_hybrid_batch(hb.shape, chunk_lens=[n_rows] if n_rows else [],
+                                 chunk_starts=[c0.start_pos + c0.length - n_rows] if n_rows else [],
+                                 n_decodes=4, ctx_range=(lo, hi), seed=1, weights=hb.weights)
+    sargs = oracle_args(sample)
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t = time.perf_counter()
+            layer_forward(*sargs)
+            t1 = time.perf_counter() - t
+        ms = sample.x.shape[0]
+        res["one_thread"] = {"value": round(ms / t1, 2), "unit": "tokens/s", "cores": 1,
+                             "sample": f"{n_rows} chunk rows after {c0.start_pos + c0.length - n_rows if c0 else 0} "
+                                       f"cached tokens + 4 decodes (ctx U[{lo},{hi}]) of the same "
+                                       f"layer and weights, M={ms}, one call {t1:.2f} s"}
+    return res
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        log("bench.py: only --gpus 1 is supported (single-GPU build)")
-        sys.exit(2)
+def measure(a, name, steps, warmup, settle_ms, graph, key):
+    """Layer time, graph replay, per-call spread, per-slot times and the
+    dominant slot's roofline for one workload."""
     import torch
     from chunked_prefill_hybrid_rmsnorm_amd import binding as B
     from chunked_prefill_hybrid_rmsnorm_amd import profiling as P
     from chunked_prefill_hybrid_rmsnorm_amd import roofline as RL
-    if not torch.cuda.is_available():
-        log("bench.py needs a GPU")
-        sys.exit(1)
-    B.load()
-    torch.cuda.set_device(0)
-
-    if a.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    log(f"generating {a.workload} inputs ...")
-    hb, desc = make_batch(a.workload)
+    log(f"generating {name} inputs ...")
+    hb, desc = make_batch(name)
     db = B.DeviceBatch(hb, pad=a.pad)
     log("uploading rotation copies ...")
     copies = [((db.wt, db.weights), db.kv)]
@@ -160,41 +200,41 @@ def main():
         B.hl_layer_forward(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws, db.ws_bytes,
                            a.pad)
 
-    log(f"layer: {a.warmup} warmup + {a.steps} timed steps ...")
-    ms = time_loop(layer, a.steps, a.warmup)
+    log(f"layer: settle {settle_ms:.0f} ms + {warmup} warmup + {steps} timed steps ...")
+    ms = time_loop(layer, steps, warmup, settle_ms)
     M = db.M
     tok_s = M / (ms / 1e3)
     log(f"layer {ms * 1e3:.1f} us/step, {tok_s / 1e6:.3f} M tokens/s")
 
-    # the same calls recorded once per rotation copy into HIP graphs and
-    # replayed: removes the host-side launch cost of the layer's kernels
-    graph = None
-    if not a.no_graph:
-        graphs = []
+    # one graph holding one call per rotation copy, replayed: the host launch
+    # cost of the layer's kernels and of the graph launch itself is spread
+    # over the calls it holds
+    g_res = None
+    if graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        for i in range(len(copies)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(len(copies)):
                 layer(i)
-            graphs.append(g)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        gms = time_loop(lambda i: graphs[i % len(graphs)].replay(), a.steps, a.warmup)
-        graph = {"ms_per_step": round(gms, 5), "value": round(M / (gms / 1e3), 1)}
-        log(f"layer (graph replay) {gms * 1e3:.1f} us/step, {M / (gms / 1e3) / 1e6:.3f} M tokens/s")
+        reps = max(1, steps // len(copies))
+        gms = time_loop(lambda i: g.replay(), reps, max(1, warmup // len(copies))) / len(copies)
+        g_res = {"ms_per_step": round(gms, 5), "value": round(M / (gms / 1e3), 1),
+                 "calls_per_graph": len(copies)}
+        log(f"layer (graph replay, {len(copies)} calls per graph) {gms * 1e3:.1f} us/step")
 
-    # spread of single calls: one event between consecutive calls (each
-    # interval holds one call plus one event record)
-    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    for i in range(a.warmup):
+    # spread of single calls: one event between consecutive calls
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(warmup):
         layer(i)
     bounds[0].record()
-    for i in range(a.steps):
+    for i in range(steps):
         layer(i)
         bounds[i + 1].record()
     torch.cuda.synchronize()
-    per_call = sorted(bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(a.steps))
+    per_call = sorted(bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(steps))
 
     def pct(q):
         return round(per_call[min(len(per_call) - 1, int(q * len(per_call)))], 2)
@@ -202,9 +242,9 @@ def main():
     spread = {"p10_us": pct(0.1), "p50_us": pct(0.5), "p90_us": pct(0.9)}
     log(f"per call: p10 {spread['p10_us']} us, p50 {spread['p50_us']} us, p90 {spread['p90_us']} us")
 
-    # per-step times inside the real layer sequence: HIP events recorded by the
-    # library between its steps, on the stream it launches on
-    log("per-step timing with stage events ...")
+    # per-slot times inside the real layer sequence: HIP events recorded by
+    # the library between its kernels, on the stream it launches on
+    log("per-slot timing with stage events ...")
     names = B.stage_names()
     ns = len(names)
 
@@ -214,11 +254,11 @@ def main():
             e.record()
         return evs
 
-    ev_sets = [make_events() for _ in range(a.steps)]
+    ev_sets = [make_events() for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(a.warmup):
+    for i in range(warmup):
         layer(i)
-    for i in range(a.steps):
+    for i in range(steps):
         (wt, ws), kv = copies[i % len(copies)]
         B.hl_layer_forward_timed(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws,
                                  db.ws_bytes, a.pad, ev_sets[i])
@@ -230,11 +270,11 @@ def main():
                                                   hb.shape.ffn, lens, starts,
                                                   [int(c) for c in hb.decodes.ctx_lens], a.pad)}
     table = {}
-    for k, name in enumerate(names):
-        t = sum(ev[k].elapsed_time(ev[k + 1]) for ev in ev_sets) / a.steps * 1e-3
-        st = stages[name]
+    for k, sname in enumerate(names):
+        t = sum(ev[k].elapsed_time(ev[k + 1]) for ev in ev_sets) / steps * 1e-3
+        st = stages[sname]
         work = st.flops > 0 or st.bytes > 0
-        table[name] = {
+        table[sname] = {
             "us": round(t * 1e6, 2),
             "bound": st.bound if work else "none (launch-shape overhead)",
             "t_roof_us": round(st.t_roof() * 1e6, 2),
@@ -242,8 +282,8 @@ def main():
             "GB/s": round(st.bytes / t / 1e9, 1) if t > 0 and work else None,
             "TFLOP/s": round(st.flops / t / 1e12, 2) if t > 0 and work else None,
         }
-        log(f"  {name:24s} {t * 1e6:8.1f} us  roof {st.t_roof() * 1e6:7.1f} us  "
-            f"({table[name]['bound']}, frac {table[name]['roof_frac']})")
+        log(f"  {sname:24s} {t * 1e6:8.1f} us  roof {st.t_roof() * 1e6:7.1f} us  "
+            f"({table[sname]['bound']}, frac {table[sname]['roof_frac']})")
     # dominant kernel: the slot with the longest average duration
     dom = max(table, key=lambda k: table[k]["us"])
     st = stages[dom]
@@ -255,31 +295,73 @@ def main():
         roof = {"bound": "mfma", "achieved": round(st.flops / t_dom / 1e12, 2),
                 "peak": RL.PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = P.stored_traffic(TRAFFIC_FILE, dom)
+    roof["traffic"] = P.stored_traffic(TRAFFIC_FILE, dom, key)
     roof["kernel"] = dom
     roof["kernel_us"] = table[dom]["us"]
     roof["algorithmic_per_launch"] = st.bytes if st.bound == "hbm" else st.flops
     roof["algorithmic_bytes"] = st.bytes
     roof["algorithmic_flops"] = st.flops
     t_roof = RL.layer_roofline_time(list(stages.values()))
-
-    result = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": desc, "rows": M, "rows_padded": db.Mp, "pad": a.pad,
-                   "rotated_copies": a.rotate},
-        "roofline": roof,
+    return hb, desc, {
+        "ms": ms, "tok_s": tok_s, "M": M, "Mp": db.Mp, "roofline": roof, "stages": table,
         "layer_roofline": {"t_roof_us": round(t_roof * 1e6, 2), "t_us": round(ms * 1e3, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
-        "stages": table,
-        "graph_replay": graph,
-        "per_call": spread,
+        "graph_replay": g_res, "per_call": spread}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("bench.py: only --gpus 1 is supported (single-GPU build)")
+        sys.exit(2)
+    import torch
+    from chunked_prefill_hybrid_rmsnorm_amd import binding as B
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    B.load()
+    torch.cuda.set_device(0)
+
+    if a.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    hb, desc, r = measure(a, a.workload, a.steps, a.warmup, a.settle_ms, not a.no_graph, a.workload)
+    extra = {}
+    for name in [w for w in a.extra.split(",") if w and w != a.workload]:
+        if name not in WORKLOADS:
+            log(f"unknown extra workload {name}")
+            sys.exit(2)
+        _, edesc, er = measure(a, name, min(a.steps, 100), min(a.warmup, 50), a.settle_ms, False,
+                               name)
+        extra[name] = {"workload": edesc, "value": round(er["tok_s"], 1), "unit": "tokens/s",
+                       "ms_per_step": round(er["ms"], 5), "rows": er["M"],
+                       "roofline": er["roofline"], "layer_roofline": er["layer_roofline"],
+                       "stages": {k: v["us"] for k, v in er["stages"].items()}}
+        torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC, "value": round(r["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "rows": r["M"], "rows_padded": r["Mp"], "pad": a.pad,
+                   "rotated_copies": a.rotate, "clock_settle_ms": a.settle_ms},
+        "roofline": r["roofline"],
+        "layer_roofline": r["layer_roofline"],
+        "stages": r["stages"],
+        "graph_replay": r["graph_replay"],
+        "per_call": r["per_call"],
+        "extra": extra,
     }
     if not a.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(hb, a.cpu_runs)
+        result["cpu_baseline"] = cpu_baseline(hb, a.workload, a.cpu_runs)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -65,20 +65,23 @@ Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad
   L.h = o;    o = align256(o + Mp * H * 2);
   L.xn2 = o;  o = align256(o + Mp * H * 2);
   L.act = o;  o = align256(o + Mp * F * 2);
+  // The attention partials (decode and prefill key splits) and the GEMMs'
+  // split-K partials share one region: the QKV partials are consumed by the
+  // RoPE step before attention writes its partials, and the merge has read
+  // those before the O projection writes its own.
   L.dec = o;
   o = align256(o + (n_dec > 0
                         ? decode_workspace_bytes(n_dec, c->n_q_heads, c->n_kv_heads, d, max_ctx)
                         : 0));
   L.pre = o;
   o = align256(o + prefill_workspace_bound(rows, c->n_q_heads, c->n_kv_heads, (int)d));
-  L.gemm = o;
+  L.gemm = L.dec;
   const int nqd = c->n_q_heads * c->head_dim;
   const size_t g = std::max({gemm_workspace_bytes(EPI_STORE, L.Mp, (int)nqkv, (int)H),
                              gemm_workspace_bytes(EPI_RESIDUAL, L.Mp, (int)H, nqd),
                              gemm_workspace_bytes(EPI_RESIDUAL, L.Mp, (int)H, (int)F),
                              gemm_workspace_bytes(EPI_SWIGLU, L.Mp, (int)F, (int)H)});
-  o = align256(o + g);
-  L.total = o;
+  L.total = std::max(o, L.gemm + align256(g));
   return L;
 }
 
@@ -97,7 +100,7 @@ size_t workspace_need(const hl_config* c, int rows, int n_dec, int max_ctx, int 
                   gemm_workspace_bytes(EPI_RESIDUAL, mp, H, nqd),
                   gemm_workspace_bytes(EPI_RESIDUAL, mp, H, F),
                   gemm_workspace_bytes(EPI_SWIGLU, mp, F, H)});
-  return L.gemm + align256(g);
+  return std::max(L.total, L.gemm + align256(g));
 }
 
 // Device address of `scratch` on the device that runs `stream`, looked up

@@ -134,7 +134,9 @@ def kernel_durations(trace_csv: str, skip: int = 0) -> Dict[str, List[float]]:
 
 def counter_values(counter_csv: str, counter: str) -> Tuple[Dict[str, List[float]], float]:
     """Per slot, the counter's value (KiB) of every dispatch, and the value of
-    the largest plain copy (the 256 MiB calibration copy)."""
+    the first plain copy: the 256 MiB calibration copy, which the profiled
+    program runs before any other copy (later copies, e.g. the rotated
+    weight clones, can be larger)."""
     lab = SlotLabeler()
     out: Dict[str, List[float]] = defaultdict(list)
     calib = 0.0
@@ -143,7 +145,8 @@ def counter_values(counter_csv: str, counter: str) -> Tuple[Dict[str, List[float
             continue
         v = float(r["Counter_Value"])
         if "copyBuffer" in r["Kernel_Name"]:
-            calib = max(calib, v)
+            if calib == 0.0:
+                calib = v
             continue
         s = lab.label(r["Kernel_Name"])
         if s:
@@ -182,7 +185,21 @@ def summarize(trace_csv: Optional[str], fetch_csv: Optional[str], write_csv: Opt
     return res
 
 
-def write_markdown(path: str, res: dict, workload: str, commands: List[str]) -> None:
+def stats_table(stats_csv: str) -> List[str]:
+    """rocprofv3's --stats summary (kernel_stats.csv) as markdown rows: every
+    kernel of the profiled run, its calls and average / min / max duration."""
+    lines = ["| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in _rows(stats_csv):
+        name = _base_name(r["Name"])
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} % |")
+    return lines
+
+
+def write_markdown(path: str, res: dict, workload: str, commands: List[str],
+                   stats_csv: Optional[str] = None) -> None:
     lines = [f"# Layer kernels, {workload}", "", "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in commands]
     lines += ["", f"Kernel sources digest: `{source_hash()}`", ""]
@@ -205,31 +222,46 @@ def write_markdown(path: str, res: dict, workload: str, commands: List[str]) -> 
         else:
             lines.append(f"| {s} | - | - | - | - | {f} | {w} |")
     lines += ["", f"Sum of slot averages: {tot:.1f} us per layer call.", ""]
+    if stats_csv:
+        lines += ["rocprofv3 `--kernel-trace --stats` summary of the traced run (every dispatch, "
+                  "the clock ramp included):", ""] + stats_table(stats_csv) + [""]
     with open(path, "w") as fh:
         fh.write("\n".join(lines))
 
 
-def write_traffic(path: str, res: dict, workload: str) -> None:
+def write_traffic(path: str, res: dict, workload: str, key: str) -> None:
+    """Store the per-slot HBM bytes of one workload under `key`, beside the
+    other workloads' entries; every entry carries the digest of the kernel
+    sources it was measured on."""
     kern = {s: {"traffic_bytes": round(e["traffic_bytes"]),
                 "fetch_bytes": round(e["fetch_bytes"]), "write_bytes": round(e["write_bytes"])}
             for s, e in res["slots"].items() if "traffic_bytes" in e}
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        t = {}
+    if "workloads" not in t:
+        t = {"workloads": {}}
+    t["workloads"][key] = {"source_sha": source_hash(), "workload": workload,
+                           "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"],
+                           "kernels": kern}
     with open(path, "w") as fh:
-        json.dump({"source_sha": source_hash(), "workload": workload,
-                   "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"],
-                   "kernels": kern}, fh, indent=1)
+        json.dump(t, fh, indent=1)
         fh.write("\n")
 
 
-def stored_traffic(path: str, slot: str) -> Optional[float]:
-    """HBM bytes per launch of `slot` from a committed measurement, or None
-    when there is none or any kernel source changed since it was taken."""
+def stored_traffic(path: str, slot: str, key: str) -> Optional[float]:
+    """HBM bytes per launch of `slot` in workload `key` from a committed
+    measurement, or None when there is none or any kernel source changed
+    since it was taken."""
     try:
         t = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_hash():
+    w = t.get("workloads", {}).get(key)
+    if not w or w.get("source_sha") != source_hash():
         return None
-    e = t.get("kernels", {}).get(slot)
+    e = w.get("kernels", {}).get(slot)
     return e.get("traffic_bytes") if e else None
 
 
@@ -300,8 +332,10 @@ def main():
     p.add_argument("--command", action="append", default=[])
     p.add_argument("--md")
     p.add_argument("--traffic")
+    p.add_argument("--key", default="mistral", help="workload key of the --traffic entry")
     p.add_argument("--skip", type=int, default=0,
                    help="drop the first N dispatches of each slot (clock ramp)")
+    p.add_argument("--stats", help="rocprofv3 kernel_stats.csv of the traced run")
     p.add_argument("--mfma", help="counter CSV of a pass over MFMA_COUNTERS")
     p.add_argument("--mfma-md")
     a = p.parse_args()
@@ -313,9 +347,9 @@ def main():
         return
     res = summarize(a.trace, a.fetch, a.write, a.skip)
     if a.md:
-        write_markdown(a.md, res, a.workload, a.command)
+        write_markdown(a.md, res, a.workload, a.command, a.stats)
     if a.traffic:
-        write_traffic(a.traffic, res, a.workload)
+        write_traffic(a.traffic, res, a.workload, a.key)
     print(json.dumps(res, indent=1))
 
 

@@ -58,7 +58,8 @@ def test_workspace_bytes_host_only(lib):
     # activations alone: xn1, xn2, h [Mp,H], qkv, attn, act, all bf16
     acts = 288 * 2 * (3 * 4096 + 6144 + 4096 + 14336)
     assert ws >= acts
-    assert ws > B.hl_workspace_bytes(cfg, 288, 0, 0, 16)
+    # decode partials share the region of the GEMM split-K partials
+    assert ws >= B.hl_workspace_bytes(cfg, 288, 0, 0, 16)
     assert B.hl_workspace_bytes(cfg, 257, 0, 0, 256) > B.hl_workspace_bytes(cfg, 257, 0, 0, 16)
 
 
