@@ -178,6 +178,7 @@ struct Choice {
   int r256;    // 1: 256-row tiles instead of 288 (fewer padded rows)
   int splits;  // K splits (1 = none)
   int wide;    // 1: 256-weight-row tile, two stages (two or more row tiles, long k loops)
+  int agpr;    // 1: SwiGLU on the one-wave-per-SIMD kernel (gemm_agpr.hip)
 };
 
 // Split K (powers of two, at most 8, at least 8 k-steps per split) while the
@@ -201,6 +202,21 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   const int mt = (mp + bm - 1) / bm;
   const int ksteps = k / kGemmBK;
   c.wide = 0;
+  c.agpr = 0;
+  if (c.big && mt >= 2 && epi == EPI_SWIGLU && ksteps >= 16) {
+    // one wave per SIMD, 112 outputs per tile, no K split: taken where its
+    // rounds of 256 workgroups are at least as full as the default tile's
+    // (Llama-2-70B-shaped gate/up: 512 workgroups, exactly two rounds)
+    const int wg = mt * ((n + 111) / 112);
+    const int dt = mt * ((n + 63) / 64);
+    const int dwg = dt * splits_for(dt, ksteps);
+    if (wg >= 192 &&
+        (long long)wg * ((dwg + 255) / 256) >= (long long)dwg * ((wg + 255) / 256)) {
+      c.agpr = 1;
+      c.splits = 1;
+      return c;
+    }
+  }
   if (c.big && mt >= 2 && epi != EPI_STORE) {
     // two or more row tiles: the MFMA work per weight byte is high enough
     // that the copies, not the weight stream, bound the k loop; a
@@ -325,6 +341,10 @@ hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf1
   if (ch.splits > 1 && ws == nullptr) ch.splits = 1;
   float* part = reinterpret_cast<float*>(ws);
   hipError_t e;
+  if (ch.agpr) {
+    if ((e = launch_swiglu_agpr(a, w, w2, c, m_padded, n, k, ch.r256, s)) != hipSuccess) return e;
+    return mid ? hipEventRecord(mid, s) : hipSuccess;
+  }
   switch (epi) {
     case EPI_STORE:
       e = run_choice<EPI_STORE>(ch, a, w, nullptr, c, nullptr, part, m, m_padded, n, k, s);

@@ -25,6 +25,11 @@ enum GemmEpilogue { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2 };
 // Launchers of two kernels record `mid` (when not null) on the stream between
 // the first and the second, also when the second is not needed.
 size_t gemm_workspace_bytes(GemmEpilogue epi, int m_padded, int n, int k);
+// act = silu(a w_gate^T) * (a w_up^T) with one wave per SIMD and the
+// accumulators in AGPRs (gemm_agpr.hip): 288- (or 256-, rows256) row tiles
+// of 112 outputs, no K split.
+hipError_t launch_swiglu_agpr(const bf16* a, const bf16* wg, const bf16* wu, bf16* act, int mp,
+                              int f, int k, bool rows256, hipStream_t s);
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
                        const bf16* residual, void* ws, int m, int m_padded, int n, int k,
                        hipStream_t s, hipEvent_t mid = nullptr);
