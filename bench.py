@@ -36,7 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "hybrid-batch tokens/s per layer (Lp+Bd); % peak MFMA (linear), % HBM BW (attn)"
-WORKLOADS = ["llama70", "mistral", "tiny", "llama70_tp8", "mistral_tp4"]
+WORKLOADS = ["llama70", "mistral", "tiny", "llama70_tp8", "mistral_tp4", "decode128"]
 
 
 def log(msg):
@@ -80,6 +80,10 @@ def make_batch(name, seed=0, **kw):
         return I.mistral_tp4_batch(seed=seed, **kw), (
             "mistral7b layer, one GPU's tensor-parallel share (T=4: 8 q / 2 kv heads, F=3584): "
             "Lp=256 (768 cached) + Bd=32 decodes, ctx U[128,2048]")
+    if name == "decode128":
+        return I.make_hybrid_batch(I.MISTRAL_7B, chunk_lens=[], chunk_starts=[], n_decodes=128,
+                                   ctx_range=(128, 4096), seed=seed, weight_std=0.02), (
+            "mistral7b-shaped layer, decodes only: Bd=128 decodes, ctx U[128,4096]")
     return I.tiny_batch(seed=seed), "tiny layer H=256: Lp=64 (64 cached) + Bd=4 decodes, ctx U[16,128]"
 
 

@@ -408,9 +408,15 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs A) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, q = lane >> 4;
   const int b = blockIdx.x;
-  if (b < A.pf_wgs)
-    prefill_block<D, NW>(A, b, wave, lane, ring);
-  else
+  if (b < A.pf_wgs) {
+    // Workgroup ids are dealt round-robin over the 8 XCDs, each with its own
+    // L2.  Prefill units are numbered kv head by kv head; XCD x takes a
+    // contiguous run of them, so with 8 kv heads all row groups of one head
+    // share one L2, which then fetches that head's keys once instead of
+    // every XCD fetching every head's keys.
+    const int per = A.pf_wgs / 8, rem = A.pf_wgs % 8, xcd = b % 8;
+    prefill_block<D, NW>(A, xcd * per + min(xcd, rem) + b / 8, wave, lane, ring);
+  } else
     decode_wave<D>(A, (b - A.pf_wgs) * NW + wave, lane, l16, q);
 }
 
@@ -559,6 +565,13 @@ void prefill_split(const ChunkList& chunks, int nq, int nkv, bool with_decodes, 
   const int aim = with_decodes ? kPfAimHybrid : kPfAimAlone;
   const int below = with_decodes ? kPfAimHybrid : kPfAimAlone / 2;
   if (base > 0 && base < below) ns = min((aim + base - 1) / base, max(1, max_keys / 256));
+  // a chunk of few row groups over a long cached prefix (a tensor-parallel
+  // share: one kv head) walks its keys in segments of at most 1024, up to the
+  // split count the workspace bound allows (Llama-2-70B-shaped T=8 share:
+  // attention 60.3 -> 37.6 us; 512-key segments were slower, their prefill
+  // workgroups crowd out the decode waves)
+  if (base > 0 && base < kPfAimAlone / 4)
+    ns = max(ns, min((max_keys + 1023) / 1024, (kPfAimAlone + base - 1) / base));
   ns = max(ns, 1);
   int sg = (max_keys + ns - 1) / ns;
   sg = (sg + 31) / 32 * 32;

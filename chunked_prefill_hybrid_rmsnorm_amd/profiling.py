@@ -185,6 +185,75 @@ def summarize(trace_csv: Optional[str], fetch_csv: Optional[str], write_csv: Opt
     return res
 
 
+def n_chunk_fetch(counter_csv: str, reps: int, kv_bytes_per_token: int, prompt: int = 2048) -> dict:
+    """HBM bytes the attention kernel reads over the N calls of a prompt
+    prefilled in N chunks (sweep --n-chunk-counters), against the closed
+    form of the re-read of earlier chunks, C N (N-1)/2 kvB.
+
+    The groups are delimited by one-element fill kernels whose order gives N
+    (1, 2, 4, 8, 16); FETCH_SIZE is scaled by the first copy of the run (256
+    MiB).  Every group reads the prompt's own KV once, its q rows and the
+    same amount of other data, so the measured re-read is the group's bytes
+    minus those of N = 1."""
+    rows = _rows(counter_csv)
+    calib = 0.0
+    groups: List[float] = []
+    lab = SlotLabeler()
+    for r in rows:
+        if r["Counter_Name"] != "FETCH_SIZE":
+            continue
+        name = r["Kernel_Name"]
+        v = float(r["Counter_Value"])
+        if "copyBuffer" in name:
+            if calib == 0.0:
+                calib = v
+            continue
+        if "FillFunctor" in name and int(r.get("Grid_Size", 0) or 0) <= 1024:
+            groups.append(0.0)
+            continue
+        if groups and lab.label(name) == "attention":
+            groups[-1] += v
+    scale = CALIBRATION_BYTES / (calib * 1024) if calib else 1.0
+    groups = groups[-5:]  # the last five markers are the N = 1 .. 16 groups
+    ns = (1, 2, 4, 8, 16)[:len(groups)]
+    per_n = {n: g * 1024 * scale / reps for n, g in zip(ns, groups)}
+    base = per_n.get(1, 0.0)
+    out = {"fetch_scale": scale, "rows": []}
+    for n in ns:
+        c = prompt // n
+        closed = c * n * (n - 1) // 2 * kv_bytes_per_token
+        meas = per_n[n] - base
+        out["rows"].append({"n": n, "chunk": c, "attention_fetch_bytes": per_n[n],
+                            "reread_measured_bytes": meas, "reread_closed_form_bytes": closed,
+                            "ratio": meas / closed if closed else None})
+    return out
+
+
+def write_n_chunk_markdown(path: str, res: dict, commands: List[str]) -> None:
+    lines = ["# KV re-read of chunked prefill, measured by counters", "",
+             "Mistral-7B-shaped layer (8 kv heads, head_dim 128: kvB = 4096 bytes of K and V per "
+             "token), a 2048-token prompt prefilled in N equal chunks over N layer calls, Bd = 0. "
+             "Chunk k reads the KV of the k chunks before it (Sarathi-Serve digest, section 4), so "
+             "the whole prompt re-reads C N(N-1)/2 tokens of KV.", "",
+             "Commands (run from the repository root):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", f"Kernel sources digest: `{source_hash()}`", "",
+              f"FETCH_SIZE scale from the 256 MiB copy: x{res['fetch_scale']:.4f}. "
+              "Measured re-read = HBM bytes the attention kernel fetched over the N calls minus "
+              "those of the N = 1 call, which reads the same prompt KV, q rows and tables once.", "",
+              "| N | chunk C | attention HBM read over the N calls, MB | re-read measured, MB | "
+              "closed form C N(N-1)/2 kvB, MB | measured / closed form |",
+              "|---:|---:|---:|---:|---:|---:|"]
+    for r in res["rows"]:
+        ratio = f"{r['ratio']:.3f}" if r["ratio"] is not None else "-"
+        lines.append(f"| {r['n']} | {r['chunk']} | {r['attention_fetch_bytes'] / 1e6:.2f} | "
+                     f"{r['reread_measured_bytes'] / 1e6:.2f} | "
+                     f"{r['reread_closed_form_bytes'] / 1e6:.2f} | {ratio} |")
+    lines.append("")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+
+
 def stats_table(stats_csv: str) -> List[str]:
     """rocprofv3's --stats summary (kernel_stats.csv) as markdown rows: every
     kernel of the profiled run, its calls and average / min / max duration."""
@@ -328,7 +397,7 @@ def main():
     p.add_argument("--trace")
     p.add_argument("--fetch")
     p.add_argument("--write")
-    p.add_argument("--workload", required=True)
+    p.add_argument("--workload", default="")
     p.add_argument("--command", action="append", default=[])
     p.add_argument("--md")
     p.add_argument("--traffic")
@@ -338,7 +407,16 @@ def main():
     p.add_argument("--stats", help="rocprofv3 kernel_stats.csv of the traced run")
     p.add_argument("--mfma", help="counter CSV of a pass over MFMA_COUNTERS")
     p.add_argument("--mfma-md")
+    p.add_argument("--n-chunk", help="FETCH_SIZE CSV of sweep --n-chunk-counters")
+    p.add_argument("--n-chunk-reps", type=int, default=5)
+    p.add_argument("--n-chunk-md")
     a = p.parse_args()
+    if a.n_chunk:
+        res = n_chunk_fetch(a.n_chunk, a.n_chunk_reps, 4096)
+        if a.n_chunk_md:
+            write_n_chunk_markdown(a.n_chunk_md, res, a.command)
+        print(json.dumps(res, indent=1))
+        return
     if a.mfma:
         res = mfma_summary(a.mfma, a.trace, a.skip)
         if a.mfma_md:

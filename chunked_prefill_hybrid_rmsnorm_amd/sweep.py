@@ -168,6 +168,33 @@ def n_chunk_prefill(pool: Pool, nc: int, reps: int) -> Dict[str, float]:
     return {"ms": ms, "attention_ms": att / reps}
 
 
+def n_chunk_counter_pass(args) -> None:
+    """The N-chunk prefill alone, for a rocprofv3 --pmc FETCH_SIZE pass.  A
+    256 MiB device copy comes first (the byte counters' scale); then, for
+    each N, one marker kernel (a one-element fill) and `seq_reps` runs of
+    the N calls, so the counter file splits into the N groups at the
+    markers."""
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    torch.empty_like(src).copy_(src)
+    torch.cuda.synchronize()
+    del src
+    pool = Pool(args.seed)
+    none = pool.decodes(0)
+    marker = torch.empty(1, dtype=torch.float32, device="cuda")
+    point(pool, 256, 0, 16, 5, 0)
+    for nc in NS:
+        marker.fill_(float(nc))
+        c = PROMPT // nc
+        for r in range(args.seq_reps):
+            for k in range(nc):
+                pool.call(r * nc + k, pool.prompt_chunk(c, k), none, pool.x[k * c:(k + 1) * c],
+                          pool.out[k * c:(k + 1) * c], 16)
+    torch.cuda.synchronize()
+    log(f"N-chunk counter pass: N in {NS}, {args.seq_reps} runs each")
+
+
 def run(args) -> dict:
     import torch
     torch.cuda.set_device(0)
@@ -234,7 +261,7 @@ def write_md(path: str, res: dict, command: str) -> None:
         a, b = res["pad_step"][f"256,{pad}"], res["pad_step"][f"257,{pad}"]
         L.append(f"| {pad} | {us(a)} | {us(b)} | {100 * (b / a - 1):+.1f} % |")
     L += ["", f"## A {PROMPT}-token prompt prefilled in N chunks", "",
-          "| N | chunk | all N calls, us | attention + merge, us | KV re-read from earlier chunks |",
+          "| N | chunk | all N calls, us | attention + merge, us | KV re-read from earlier chunks, closed form C N(N-1)/2 kvB |",
           "|---:|---:|---:|---:|---:|"]
     for nc in NS:
         r = res["n_chunks"][str(nc)]
@@ -264,7 +291,12 @@ def main():
     p.add_argument("--seq-reps", type=int, default=5)
     p.add_argument("--md", help="write the tables as markdown here")
     p.add_argument("--json", help="write the raw numbers here")
+    p.add_argument("--n-chunk-counters", action="store_true",
+                   help="only run the N-chunk prefill, marked for a FETCH_SIZE counter pass")
     a = p.parse_args()
+    if a.n_chunk_counters:
+        n_chunk_counter_pass(a)
+        return
     res = run(a)
     cmd = "python -m chunked_prefill_hybrid_rmsnorm_amd.sweep " + " ".join(sys.argv[1:])
     if a.md:
