@@ -9,8 +9,13 @@ fits one GPU unsharded.  Synthetic, seeded inputs (seed 0).  The
 Mistral-7B-shaped layer (Lp=256 after 768 cached + Bd=32 decodes,
 contexts U{128..2048}) is timed briefly beside it (`extra`).
 
-A step is one ``hl_layer_forward`` call (every kernel of the layer).  Inputs
-are resident in HBM before the timed region; R copies of the weights and of
+A step is one layer call as it runs inside a stack of layers
+(``hl_layer_forward_chain``): every kernel of the layer, with the layer's
+input RMSNorm already formed by the previous layer's down-projection reduce
+and this call's reduce forming the next layer's -- one RMSNorm per call, as
+in the stand-alone ``hl_layer_forward``, which is timed beside it
+(`standalone_call`; ``--plain`` makes it the timed step).  Inputs are
+resident in HBM before the timed region; R copies of the weights and of
 the KV pool are rotated so that the 256 MB MALL cannot hold one call's
 working set for the next.  Before the W warmup steps the layer runs for
 about --settle-ms of GPU time so that the clocks have left their ramp (the
@@ -58,6 +63,10 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-runs", type=int, default=1)
+    p.add_argument("--no-standalone", action="store_true",
+                   help="skip the stand-alone call's timing (profiling runs)")
+    p.add_argument("--plain", action="store_true",
+                   help="time the stand-alone layer call instead of the call inside a stack")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 256 MiB device-to-device copy first (PMC byte-counter scale)")
     return p.parse_args()
@@ -199,10 +208,26 @@ def measure(a, name, steps, warmup, settle_ms, graph, key):
         copies.append(((wt, wstruct), B.hl_kv(kvt.data_ptr(), db.kv.num_pages)))
     torch.cuda.synchronize()
 
-    def layer(i):
+    # a layer inside a stack: its input RMSNorm (xn_in) was formed by the
+    # previous layer's down-projection reduce, and its own reduce forms the
+    # next layer's (xn_next) -- one RMSNorm per call, as in the plain call
+    H = hb.shape.hidden
+    xn_in = torch.empty((db.Mp, H), dtype=torch.bfloat16, device="cuda")
+    B.hl_rmsnorm(db.x, db.wt["g_attn"], xn_in, db.M, db.Mp, H, hb.shape.rms_eps)
+    xn_next = torch.empty_like(xn_in)
+
+    def plain(i):
         (wt, ws), kv = copies[i % len(copies)]
         B.hl_layer_forward(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws, db.ws_bytes,
                            a.pad)
+
+    def chained(i, events=None):
+        (wt, ws), kv = copies[i % len(copies)]
+        B.hl_layer_forward_chain(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws,
+                                 db.ws_bytes, a.pad, xn_in=xn_in, g_next=wt["g_attn"],
+                                 xn_next=xn_next, events=events)
+
+    layer = plain if a.plain else chained
 
     log(f"layer: settle {settle_ms:.0f} ms + {warmup} warmup + {steps} timed steps ...")
     ms = time_loop(layer, steps, warmup, settle_ms)
@@ -263,16 +288,20 @@ def measure(a, name, steps, warmup, settle_ms, graph, key):
     for i in range(warmup):
         layer(i)
     for i in range(steps):
-        (wt, ws), kv = copies[i % len(copies)]
-        B.hl_layer_forward_timed(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws,
-                                 db.ws_bytes, a.pad, ev_sets[i])
+        if a.plain:
+            (wt, ws), kv = copies[i % len(copies)]
+            B.hl_layer_forward_timed(db.cfg, ws, db.x, db.chunks, db.dec, kv, db.out, db.ws,
+                                     db.ws_bytes, a.pad, ev_sets[i])
+        else:
+            chained(i, ev_sets[i])
     torch.cuda.synchronize()
     lens = [c.length for c in hb.chunks]
     starts = [c.start_pos for c in hb.chunks]
     stages = {s.name: s for s in RL.layer_stages(hb.shape.hidden, hb.shape.n_q_heads,
                                                   hb.shape.n_kv_heads, hb.shape.head_dim,
                                                   hb.shape.ffn, lens, starts,
-                                                  [int(c) for c in hb.decodes.ctx_lens], a.pad)}
+                                                  [int(c) for c in hb.decodes.ctx_lens], a.pad,
+                                                  chained=not a.plain)}
     table = {}
     for k, sname in enumerate(names):
         t = sum(ev[k].elapsed_time(ev[k + 1]) for ev in ev_sets) / steps * 1e-3
@@ -306,11 +335,17 @@ def measure(a, name, steps, warmup, settle_ms, graph, key):
     roof["algorithmic_bytes"] = st.bytes
     roof["algorithmic_flops"] = st.flops
     t_roof = RL.layer_roofline_time(list(stages.values()))
+    other = None
+    if not a.plain and not a.no_standalone:
+        # the stand-alone call (its own first RMSNorm, no next-layer norm)
+        pms = time_loop(plain, max(steps // 2, 1), max(warmup // 2, 1))
+        other = {"ms_per_step": round(pms, 5), "value": round(M / (pms / 1e3), 1)}
+        log(f"stand-alone call (own first RMSNorm) {pms * 1e3:.1f} us/step")
     return hb, desc, {
         "ms": ms, "tok_s": tok_s, "M": M, "Mp": db.Mp, "roofline": roof, "stages": table,
         "layer_roofline": {"t_roof_us": round(t_roof * 1e6, 2), "t_us": round(ms * 1e3, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
-        "graph_replay": g_res, "per_call": spread}
+        "graph_replay": g_res, "per_call": spread, "standalone_call": other}
 
 
 def main():
@@ -355,12 +390,16 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "rows": r["M"], "rows_padded": r["Mp"], "pad": a.pad,
-                   "rotated_copies": a.rotate, "clock_settle_ms": a.settle_ms},
+                   "rotated_copies": a.rotate, "clock_settle_ms": a.settle_ms,
+                   "layer_call": ("stand-alone (own first RMSNorm)" if a.plain else
+                                  "inside a layer stack: first RMSNorm formed by the previous "
+                                  "layer's down reduce, this call's reduce forms the next one")},
         "roofline": r["roofline"],
         "layer_roofline": r["layer_roofline"],
         "stages": r["stages"],
         "graph_replay": r["graph_replay"],
         "per_call": r["per_call"],
+        "standalone_call": r["standalone_call"],
         "extra": extra,
     }
     if not a.no_cpu_baseline:

@@ -5,8 +5,9 @@ Every iteration: the scheduler forms the batch (decodes first, then prompt
 chunks within the token budget); the library embeds the rows' input tokens
 (prompt ids, or each decoding request's last generated token, kept on the
 GPU), runs the L layer calls (each layer with its own page pool, all sharing
-the block tables), the final RMSNorm, the LM head GEMM and the greedy choice
-of the rows that yield a token.  The host only counts tokens: the generated
+the block tables; each layer's input RMSNorm is formed by the previous
+layer's last kernel, and the last layer's forms the final RMSNorm), the LM
+head GEMM and the greedy choice of the rows that yield a token.  The host only counts tokens: the generated
 ids stay on the GPU until the end (there is no end-of-sequence token), so the
 host can queue iterations ahead of the GPU.
 
@@ -130,7 +131,10 @@ class BatchingLoop:
         H, V = s.hidden, model.vocab
         self.x = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
         self.y = torch.empty_like(self.x)
-        self.xn = torch.empty((self.Mp_max, H), dtype=torch.bfloat16, device="cuda")
+        # normalised layer inputs, handed from one layer call to the next
+        # (cross-layer RMSNorm fusion); the last holds the final norm
+        self.xn = [torch.empty((self.Mp_max, H), dtype=torch.bfloat16, device="cuda")
+                   for _ in range(2)]
         self.logits = torch.empty((self.Mp_max, V), dtype=torch.bfloat16, device="cuda")
         max_ctx = max(len(p) for p in self.prompts) + gen_len
         self.ws_bytes = B.hl_workspace_bytes(model.cfg, rows, n_req, max_ctx, pad)
@@ -188,12 +192,17 @@ class BatchingLoop:
             e0.record()
             x, y = self.x[:M], self.y[:M]
             B.hl_embed_rows(m.table, m.vocab, s.hidden, ids_d, self.last_tok, M, x)
-            for (_, w), kv in zip(m.layers, self.kv):
-                B.hl_layer_forward(m.cfg, w, x, chunks, dec, kv, y, self.ws, self.ws_bytes,
-                                   self.pad)
+            # layer l's first RMSNorm comes from layer l-1's down-projection
+            # reduce; the last layer's reduce forms the final norm
+            xa, xb = self.xn
+            B.hl_rmsnorm(x, m.layers[0][0]["g_attn"], xa, M, Mp, s.hidden, s.rms_eps)
+            for l, ((_, w), kv) in enumerate(zip(m.layers, self.kv)):
+                g_next = m.layers[l + 1][0]["g_attn"] if l + 1 < len(m.layers) else m.g_final
+                B.hl_layer_forward_chain(m.cfg, w, x, chunks, dec, kv, y, self.ws, self.ws_bytes,
+                                         self.pad, xn_in=xa, g_next=g_next, xn_next=xb)
                 x, y = y, x
-            B.hl_rmsnorm(x, m.g_final, self.xn, M, Mp, s.hidden, s.rms_eps)
-            B.hl_gemm_bf16(self.xn, m.lm, self.logits, None, Mp, Mp, m.vocab, s.hidden,
+                xa, xb = xb, xa
+            B.hl_gemm_bf16(xa, m.lm, self.logits, None, Mp, Mp, m.vocab, s.hidden,
                            self.gws, self.gws_bytes)
             B.hl_argmax_rows(self.logits, M, m.vocab, sreq_d, spos_d, self.last_tok,
                              self.out_tokens)

@@ -63,6 +63,10 @@ class hl_taps(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("xn1", "qkv", "attn", "h", "xn2", "act")]
 
 
+class hl_chain(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("xn_in", "g_next", "xn_next")]
+
+
 _P = ctypes.POINTER
 _c = ctypes
 _SIGS = {
@@ -79,6 +83,11 @@ _SIGS = {
                                           _P(hl_chunk), _c.c_int32, _P(hl_decodes), _P(hl_kv),
                                           _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int32,
                                           _P(hl_taps), _P(_c.c_void_p), _c.c_void_p]),
+    "hl_layer_forward_chain": (_c.c_int, [_P(hl_config), _P(hl_weights), _c.c_void_p,
+                                          _P(hl_chunk), _c.c_int32, _P(hl_decodes), _P(hl_kv),
+                                          _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int32,
+                                          _P(hl_taps), _P(hl_chain), _P(_c.c_void_p),
+                                          _c.c_void_p]),
     "hl_layer_forward_noalloc": (_c.c_int, [_P(hl_config), _P(hl_weights), _c.c_void_p,
                                             _P(hl_chunk), _c.c_int32, _P(hl_decodes), _P(hl_kv),
                                             _c.c_void_p, _c.c_int32, _P(hl_taps), _c.c_void_p]),
@@ -265,6 +274,27 @@ def hl_layer_forward_timed(cfg, weights: hl_weights, x, chunks, dec: hl_decodes,
                                        ctypes.byref(taps) if taps is not None else None, handles,
                                        _stream(stream))
     _check(rc, "hl_layer_forward_timed")
+
+
+def hl_layer_forward_chain(cfg, weights: hl_weights, x, chunks, dec: hl_decodes, kv: hl_kv, out,
+                           ws, ws_bytes: int, pad: int, xn_in=None, g_next=None, xn_next=None,
+                           events=None, taps=None, stream=None):
+    """The layer call with the cross-layer RMSNorm fusion: ``xn_in`` (this
+    layer's normalised input, from the previous call's ``xn_next``) replaces
+    the layer's own first RMSNorm; with ``g_next`` the down projection's
+    reduce also writes RMSNorm(out) * g_next into ``xn_next``.  ``events``:
+    None or N_STAGES + 1 torch.cuda.Event objects."""
+    arr, n = _chunk_array(chunks)
+    chain = hl_chain(_ptr(xn_in), _ptr(g_next), _ptr(xn_next))
+    handles = None
+    if events is not None:
+        handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    rc = load().hl_layer_forward_chain(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x), arr, n,
+                                       ctypes.byref(dec), ctypes.byref(kv), _ptr(out), _ptr(ws),
+                                       ws_bytes, pad,
+                                       ctypes.byref(taps) if taps is not None else None,
+                                       ctypes.byref(chain), handles, _stream(stream))
+    _check(rc, "hl_layer_forward_chain")
 
 
 def hl_slot_mapping(cfg, chunks, dec, num_pages, positions, slots, stream=None):

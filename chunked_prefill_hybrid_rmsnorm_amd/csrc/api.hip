@@ -35,6 +35,8 @@ int check_config(const hl_config* c) {
   if (c->n_q_heads % c->n_kv_heads) return HL_ERR_SHAPE;
   if (c->n_q_heads / c->n_kv_heads > 16) return HL_ERR_UNSUPPORTED;
   if (c->hidden % 64 || c->ffn % 64 || (c->n_q_heads * c->head_dim) % 64) return HL_ERR_SHAPE;
+  // the row-wise RMSNorm kernels hold a row in the registers of 256 threads
+  if (c->hidden > 16384) return HL_ERR_UNSUPPORTED;
   // the GEMM copies address each weight matrix by 32-bit byte offsets
   const size_t nqkv = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
   if (std::max({nqkv, (size_t)c->ffn, (size_t)c->n_q_heads * c->head_dim}) * c->hidden * 2 >
@@ -45,7 +47,7 @@ int check_config(const hl_config* c) {
 
 struct Layout {
   int Mp;
-  size_t pos, slot, cs, sn, xn1, qkv, attn, h, xn2, act, dec, pre, gemm, total;
+  size_t xn1, qkv, attn, h, xn2, act, dec, pre, gemm, total;
 };
 
 Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad) {
@@ -55,10 +57,6 @@ Layout make_layout(const hl_config* c, int rows, int n_dec, int max_ctx, int pad
   const size_t H = c->hidden, F = c->ffn, d = c->head_dim;
   const size_t nqkv = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * d;
   size_t o = 0;
-  L.pos = o;  o = align256(o + Mp * 4);
-  L.slot = o; o = align256(o + Mp * 4);
-  L.cs = o;   o = align256(o + Mp * (d / 2) * 4);
-  L.sn = o;   o = align256(o + Mp * (d / 2) * 4);
   L.xn1 = o;  o = align256(o + Mp * H * 2);
   L.qkv = o;  o = align256(o + Mp * nqkv * 2);
   L.attn = o; o = align256(o + Mp * c->n_q_heads * d * 2);
@@ -209,8 +207,8 @@ const char* hl_stage_name(int stage) {
 static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
                               const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
                               const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes,
-                              int32_t pad, const hl_taps* taps, hipStream_t stream,
-                              hipEvent_t* ev) {
+                              int32_t pad, const hl_taps* taps, const hl_chain* chain,
+                              hipStream_t stream, hipEvent_t* ev) {
   int e = check_config(cfg);
   if (e) return e;
   if (!w || !x || !kv || !out || !ws || !kv->data) return HL_ERR_NULL;
@@ -218,6 +216,13 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
     return HL_ERR_NULL;
   if (pad <= 0 || pad % 16 || kv->num_pages <= 0) return HL_ERR_SHAPE;
   if ((const void*)x == (const void*)out) return HL_ERR_SHAPE;
+  const hl_chain no_chain{};
+  const hl_chain& chn = chain ? *chain : no_chain;
+  if (chn.g_next && !chn.xn_next) return HL_ERR_NULL;
+  if (chn.g_next && ((const void*)chn.xn_next == (const void*)x ||
+                     (const void*)chn.xn_next == (const void*)out ||
+                     (const void*)chn.xn_next == (const void*)chn.xn_in))
+    return HL_ERR_SHAPE;
   ChunkList cl;
   if ((e = fill_chunks(chunks, n_chunks, &cl))) return e;
   DecDev dd;
@@ -269,12 +274,13 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
     if (!mark()) return HL_ERR_HIP; \
   } while (0)
   HL_MARK();
-  // RMSNorm of the input rows (pad rows -> 0); each row's position, KV slot
-  // and RoPE cos / sin go to a table for the append step
-  const RopeTab tab{reinterpret_cast<int32_t*>(base + L.pos), reinterpret_cast<int32_t*>(base + L.slot),
-                    reinterpret_cast<float*>(base + L.cs), reinterpret_cast<float*>(base + L.sn)};
-  HL_TRY(launch_rmsnorm_rope_table(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
-                                   cfg->rms_eps, cl, dd, kvd, d, cfg->rope_theta, tab, stream));
+  // RMSNorm of the input rows (pad rows -> 0), unless the previous layer's
+  // down-projection reduce already left it in chain->xn_in
+  if (chn.xn_in)
+    xn1 = const_cast<bf16*>(reinterpret_cast<const bf16*>(chn.xn_in));
+  else
+    HL_TRY(launch_rmsnorm(xin, reinterpret_cast<const bf16*>(w->g_attn), xn1, M, Mp, H,
+                          cfg->rms_eps, stream));
   HL_MARK();
   // fused QKV projection on the stacked rows; with split K its partials are
   // summed by the RoPE / append kernel that follows
@@ -289,7 +295,8 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
   HL_MARK();
   // each row's position and KV slot, RoPE on q and k, append K and V
   HL_TRY(launch_rope_append_wide(qkv, qkv_splits > 1 ? reinterpret_cast<const float*>(gws) : nullptr,
-                                 qkv_splits, M, Mp, nq, nkv, d, kvd, tab, stream));
+                                 qkv_splits, M, Mp, nq, nkv, d, cfg->rope_theta, cl, dd, kvd,
+                                 stream));
   HL_MARK();
   // chunk-prefill attention (rows [0, Lp)) and paged decode attention
   // (rows [Lp, M)) in one launch
@@ -306,9 +313,17 @@ static int layer_forward_impl(const hl_config* cfg, const hl_weights* w, const h
                      reinterpret_cast<const bf16*>(w->w_up), act, nullptr, gws, M, Mp, F, H,
                      stream, mid()));
   HL_MARK();
-  // down projection + residual
-  HL_TRY(launch_gemm(EPI_RESIDUAL, act, reinterpret_cast<const bf16*>(w->w_down), nullptr,
-                     reinterpret_cast<bf16*>(out), h, gws, M, Mp, H, F, stream, mid()));
+  // down projection + residual; with chain->g_next the split-K reduce also
+  // forms the next RMSNorm of the output rows (the next layer's input norm)
+  if (chn.g_next)
+    HL_TRY(launch_gemm_residual_norm(act, reinterpret_cast<const bf16*>(w->w_down),
+                                     reinterpret_cast<bf16*>(out), h,
+                                     reinterpret_cast<const bf16*>(chn.g_next),
+                                     reinterpret_cast<bf16*>(chn.xn_next), cfg->rms_eps, gws, M,
+                                     Mp, H, F, stream, mid()));
+  else
+    HL_TRY(launch_gemm(EPI_RESIDUAL, act, reinterpret_cast<const bf16*>(w->w_down), nullptr,
+                       reinterpret_cast<bf16*>(out), h, gws, M, Mp, H, F, stream, mid()));
   HL_MARK();
 #undef HL_MARK
 #undef HL_TRY
@@ -320,7 +335,19 @@ int hl_layer_forward(const hl_config* cfg, const hl_weights* w, const hl_bf16* x
                      const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
                      const hl_taps* taps, hipStream_t stream) {
   return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws, ws_bytes, pad, taps,
-                            stream, nullptr);
+                            nullptr, stream, nullptr);
+}
+
+int hl_layer_forward_chain(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                           const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                           const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
+                           const hl_taps* taps, const hl_chain* chain, hipEvent_t* stage_events,
+                           hipStream_t stream) {
+  if (stage_events)
+    for (int i = 0; i <= HL_N_STAGES; ++i)
+      if (!stage_events[i]) return HL_ERR_NULL;
+  return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws, ws_bytes, pad, taps,
+                            chain, stream, stage_events);
 }
 
 int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
@@ -331,7 +358,7 @@ int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_b
   for (int i = 0; i <= HL_N_STAGES; ++i)
     if (!stage_events[i]) return HL_ERR_NULL;
   return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws, ws_bytes, pad, taps,
-                            stream, stage_events);
+                            nullptr, stream, stage_events);
 }
 
 int hl_layer_forward_noalloc(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
@@ -354,7 +381,7 @@ int hl_layer_forward_noalloc(const hl_config* cfg, const hl_weights* w, const hl
   void* ws = nullptr;
   if ((e = scratch_address(stream, &ws))) return e;
   return layer_forward_impl(cfg, w, x, chunks, n_chunks, dec, kv, out, ws,
-                            (size_t)HL_NOALLOC_SCRATCH_BYTES, pad, taps, stream, nullptr);
+                            (size_t)HL_NOALLOC_SCRATCH_BYTES, pad, taps, nullptr, stream, nullptr);
 }
 
 int hl_slot_mapping(const hl_config* cfg, const hl_chunk* chunks, int32_t n_chunks,

@@ -59,23 +59,13 @@ struct RopeFreq {
   double inv[kRopeMaxPairs];
 };
 
-struct RopeTab {
-  int32_t* pos;
-  int32_t* slot;
-  float* cs;  // [rows][d/2]
-  float* sn;
-};
-// First RMSNorm of the layer, which also fills the rows' RoPE table.
-hipError_t launch_rmsnorm_rope_table(const bf16* x, const bf16* g, bf16* y, int rows,
-                                     int rows_padded, int hidden, float eps,
-                                     const ChunkList& chunks, const DecDev& dec, const KvDev& kv,
-                                     int d, float theta, const RopeTab& tab, hipStream_t s);
-// RoPE on q / k and KV append from the table; with `part` (split-K partials of
-// the QKV projection, `splits` planes of Mp rows) the rows are first formed
-// from them and rows [rows, Mp) of qkv are zeroed.
+// RoPE on q / k and KV append, each row's position, slot and cos / sin
+// resolved in the kernel; with `part` (split-K partials of the QKV
+// projection, `splits` planes of Mp rows) the rows are first formed from them
+// and rows [rows, Mp) of qkv are zeroed.
 hipError_t launch_rope_append_wide(bf16* qkv, const float* part, int splits, int rows, int Mp,
-                                   int nq, int nkv, int d, const KvDev& kv, const RopeTab& tab,
-                                   hipStream_t s);
+                                   int nq, int nkv, int d, float theta, const ChunkList& chunks,
+                                   const DecDev& dec, const KvDev& kv, hipStream_t s);
 
 // ws (prefill_workspace_bytes) holds key-split partials; nullptr: no split.
 size_t prefill_workspace_bytes(const ChunkList& chunks, int nq, int nkv, int d);

@@ -53,102 +53,78 @@ hipError_t launch_slot_map(const ChunkList& chunks, const DecDev& dec, int page_
 }
 
 // ----------------------------------------------------------------- RMSNorm
-// One wave per row, four rows per workgroup; the row stays in registers
-// between the sum of squares and the scaling (one global read).  hidden is a
-// multiple of 64 and at most 64 * 8 * kNormMaxChunks.
-constexpr int kNormRowsPerBlock = 4;
-constexpr int kNormMaxChunks = 32;  // 16-byte chunks per lane: hidden <= 16384
-
-// One row per wave, in two halves so that a caller can put other work
-// between issuing the loads and using them: the row and the gain vector are
-// loaded together (one memory round trip), then reduced, scaled and stored.
-template <int CH>
-struct NormRow {
-  u32x4 v[CH], g[CH];
-};
+// One 256-thread workgroup per row: each thread loads its CH 16-byte chunks
+// of the row and of the gain together (one memory round trip), the sum of
+// squares is reduced over the workgroup, and the scaled row is stored from
+// registers.  One row per workgroup keeps hundreds of workgroups in flight
+// even for a few hundred rows.  hidden is a multiple of 8 and at most
+// 256 * 8 * kNormMaxChunks.
+constexpr int kNormThreads = 256;
+constexpr int kNormMaxChunks = 8;  // 16-byte chunks per thread: hidden <= 16384
 
 template <int CH>
-__device__ __forceinline__ void rmsnorm_load(NormRow<CH>& n, const bf16* __restrict__ xr,
-                                             const bf16* __restrict__ g, int hidden, int lane) {
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
+    int hidden, float eps) {
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  bf16* yr = y + (size_t)r * hidden;
+  if (r >= rows) {  // padding row: zero dummy token
+    for (int c = tid * 8; c < hidden; c += kNormThreads * 8)
+      *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
+    return;
+  }
+  const bf16* xr = x + (size_t)r * hidden;
+  u32x4 v[CH], gv[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = (i * 64 + lane) * 8;
-    n.v[i] = c < hidden ? ld16(xr + c) : u32x4{0, 0, 0, 0};
-    n.g[i] = c < hidden ? ld16(g + c) : u32x4{0, 0, 0, 0};
+    const int c = (i * kNormThreads + tid) * 8;
+    v[i] = c < hidden ? ld16(xr + c) : u32x4{0, 0, 0, 0};
+    gv[i] = c < hidden ? ld16(g + c) : u32x4{0, 0, 0, 0};
   }
-}
-
-template <int CH>
-__device__ __forceinline__ void rmsnorm_finish(const NormRow<CH>& n, bf16* __restrict__ yr,
-                                               int hidden, float eps, int lane) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < CH; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = __uint_as_float(n.v[i][e] << 16), b = __uint_as_float(n.v[i][e] & 0xffff0000u);
+      const float a = __uint_as_float(v[i][e] << 16), b = __uint_as_float(v[i][e] & 0xffff0000u);
       ss += a * a + b * b;
     }
+  __shared__ float red[kNormThreads / 64];
   ss = wave_sum(ss);
-  const float inv = rsqrtf(ss / (float)hidden + eps);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)hidden + eps);
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = (i * 64 + lane) * 8;
+    const int c = (i * kNormThreads + tid) * 8;
     if (c >= hidden) continue;
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = __uint_as_float(n.v[i][e] << 16) * inv * __uint_as_float(n.g[i][e] << 16);
-      const float b = __uint_as_float(n.v[i][e] & 0xffff0000u) * inv *
-                      __uint_as_float(n.g[i][e] & 0xffff0000u);
+      const float a = __uint_as_float(v[i][e] << 16) * inv * __uint_as_float(gv[i][e] << 16);
+      const float b = __uint_as_float(v[i][e] & 0xffff0000u) * inv *
+                      __uint_as_float(gv[i][e] & 0xffff0000u);
       o[e] = pack2(a, b);
     }
     *reinterpret_cast<u32x4*>(yr + c) = o;
   }
 }
 
-template <int CH>
-__device__ __forceinline__ void rmsnorm_row(const bf16* __restrict__ xr, const bf16* __restrict__ g,
-                                            bf16* __restrict__ yr, int hidden, float eps, int lane) {
-  NormRow<CH> n;
-  rmsnorm_load<CH>(n, xr, g, hidden, lane);
-  rmsnorm_finish<CH>(n, yr, hidden, eps, lane);
-}
-
-template <int CH>
-__global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_kernel(
-    const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
-    int rows_padded, int hidden, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * kNormRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (r >= rows_padded) return;
-  bf16* yr = y + (size_t)r * hidden;
-  if (r >= rows) {  // padding row: zero dummy token
-    for (int c = lane * 8; c < hidden; c += 64 * 8) *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
-    return;
-  }
-  rmsnorm_row<CH>(x + (size_t)r * hidden, g, yr, hidden, eps, lane);
-}
-
-template <int CH>
-static void launch_norm(const bf16* x, const bf16* g, bf16* y, int rows, int rows_padded,
-                        int hidden, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel<CH>,
-                     dim3((rows_padded + kNormRowsPerBlock - 1) / kNormRowsPerBlock),
-                     dim3(64 * kNormRowsPerBlock), 0, s, x, g, y, rows, rows_padded, hidden, eps);
-}
-
 hipError_t launch_rmsnorm(const bf16* x, const bf16* g, bf16* y, int rows, int rows_padded,
                           int hidden, float eps, hipStream_t s) {
   if (rows_padded == 0) return hipSuccess;
-  const int ch = (hidden + 511) / 512;  // 16-byte chunks per lane
-  if (ch <= 1) launch_norm<1>(x, g, y, rows, rows_padded, hidden, eps, s);
-  else if (ch <= 2) launch_norm<2>(x, g, y, rows, rows_padded, hidden, eps, s);
-  else if (ch <= 4) launch_norm<4>(x, g, y, rows, rows_padded, hidden, eps, s);
-  else if (ch <= 8) launch_norm<8>(x, g, y, rows, rows_padded, hidden, eps, s);
-  else if (ch <= 16) launch_norm<16>(x, g, y, rows, rows_padded, hidden, eps, s);
-  else if (ch <= kNormMaxChunks) launch_norm<kNormMaxChunks>(x, g, y, rows, rows_padded, hidden, eps, s);
+  if (hidden % 8) return hipErrorInvalidValue;
+  const int ch = (hidden + kNormThreads * 8 - 1) / (kNormThreads * 8);  // chunks per thread
+  const dim3 grid(rows_padded), block(kNormThreads);
+#define HL_NORM(CH_) \
+  hipLaunchKernelGGL(rmsnorm_kernel<CH_>, grid, block, 0, s, x, g, y, rows, hidden, eps)
+  if (ch <= 1) HL_NORM(1);
+  else if (ch <= 2) HL_NORM(2);
+  else if (ch <= 4) HL_NORM(4);
+  else if (ch <= kNormMaxChunks) HL_NORM(kNormMaxChunks);
   else return hipErrorInvalidValue;
+#undef HL_NORM
   return hipGetLastError();
 }
 
@@ -256,64 +232,7 @@ hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* s
   return hipGetLastError();
 }
 
-// ---------------------------------------------------- layer path: table + wide append
-// The first RMSNorm kernel also resolves every row's position and KV slot and
-// tabulates its RoPE cos / sin, so the append kernel that follows the QKV
-// projection is pure element-wise work spread over (row, 4 heads) groups.
-template <int CH>
-__global__ __launch_bounds__(64 * kNormRowsPerBlock) void rmsnorm_rope_table_kernel(
-    const bf16* __restrict__ x, const bf16* __restrict__ g, bf16* __restrict__ y, int rows,
-    int rows_padded, int hidden, float eps, ChunkList chunks, DecDev dec, int page_size,
-    int num_pages, int d, RopeFreq freq, RopeTab tab) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * kNormRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (r >= rows_padded) return;
-  bf16* yr = y + (size_t)r * hidden;
-  if (r >= rows) {  // padding row: zero dummy token
-    for (int c = lane * 8; c < hidden; c += 64 * 8) *reinterpret_cast<u32x4*>(yr + c) = u32x4{0, 0, 0, 0};
-    return;
-  }
-  // the row's loads go out first; the table is worked out while they are in flight
-  NormRow<CH> n;
-  rmsnorm_load<CH>(n, x + (size_t)r * hidden, g, hidden, lane);
-  int pos, slot;
-  row_pos_slot(chunks, dec, page_size, num_pages, r, &pos, &slot);
-  if (lane == 0) {
-    tab.pos[r] = pos;
-    tab.slot[r] = slot;
-  }
-  const int half = d >> 1;
-  if (lane < half)
-    rope_cos_sin(pos, freq.inv[lane], tab.cs + (size_t)r * half + lane,
-                 tab.sn + (size_t)r * half + lane);
-  rmsnorm_finish<CH>(n, yr, hidden, eps, lane);
-}
-
-hipError_t launch_rmsnorm_rope_table(const bf16* x, const bf16* g, bf16* y, int rows,
-                                     int rows_padded, int hidden, float eps,
-                                     const ChunkList& chunks, const DecDev& dec, const KvDev& kv,
-                                     int d, float theta, const RopeTab& tab, hipStream_t s) {
-  if (rows_padded == 0) return hipSuccess;
-  if (d / 2 > kRopeMaxPairs) return hipErrorInvalidValue;
-  const RopeFreq freq = rope_freq(d, theta);
-  const dim3 grid((rows_padded + kNormRowsPerBlock - 1) / kNormRowsPerBlock);
-  const dim3 block(64 * kNormRowsPerBlock);
-#define HL_LAUNCH_TAB(CH_)                                                                    \
-  hipLaunchKernelGGL(rmsnorm_rope_table_kernel<CH_>, grid, block, 0, s, x, g, y, rows,        \
-                     rows_padded, hidden, eps, chunks, dec, kv.page_size, kv.num_pages, d,   \
-                     freq, tab)
-  const int ch = (hidden + 511) / 512;  // 16-byte chunks per lane
-  if (ch <= 1) HL_LAUNCH_TAB(1);
-  else if (ch <= 2) HL_LAUNCH_TAB(2);
-  else if (ch <= 4) HL_LAUNCH_TAB(4);
-  else if (ch <= 8) HL_LAUNCH_TAB(8);
-  else if (ch <= 16) HL_LAUNCH_TAB(16);
-  else if (ch <= kNormMaxChunks) HL_LAUNCH_TAB(kNormMaxChunks);
-  else return hipErrorInvalidValue;
-#undef HL_LAUNCH_TAB
-  return hipGetLastError();
-}
-
+// ---------------------------------------------------- layer path: wide append
 // 8 consecutive values of a row starting at column c, as bf16: from the bf16
 // row (SPLITS = 0), or summed over SPLITS split-K partials in split order and
 // rounded exactly as the separate reduce does (all loads issued first)
@@ -338,19 +257,23 @@ __device__ __forceinline__ u32x4 row8(const bf16* row, const float* part, size_t
   }
 }
 
-constexpr int kRopeHeads = 4;  // heads per workgroup of the wide append kernel
+constexpr int kRopeHeads = 16;     // heads per workgroup of the wide append kernel
+constexpr int kRopeThreads = 256;
 
-// Workgroup (row r, heads 4 y .. 4 y + 3) of the q, k, v heads.  q / k heads:
-// a thread takes 8 consecutive pairs, rotates them with the row's table and
-// writes them back (k also to the row's KV slot).  v heads: a thread takes 8
-// values and writes them to the slot (dimension-major in the page).  With
-// partials (SPLITS > 0 of them) the row is formed from them and written back
-// whole, and rows in [rows, Mp) are zero rows.
+// Workgroup (row r, heads 16 y .. 16 y + 15) of the q, k, v heads, one 8-wide
+// item per thread: a q / k item is 8 consecutive rotation pairs of one head
+// (rotated and written back, k also to the row's KV slot), a v item 8 values
+// of one head (written to the slot, dimension-major in the page).  The row's
+// position and slot are resolved in the workgroup and its cos / sin are
+// formed while the row's loads are in flight (one pair per thread of the
+// first d/2).  With partials (SPLITS > 0 of them) the row is formed from them
+// and written back whole, and rows in [rows, Mp) are zero rows.
 template <int SPLITS>
-__global__ __launch_bounds__(64) void rope_append_wide_kernel(
+__global__ __launch_bounds__(kRopeThreads) void rope_append_wide_kernel(
     bf16* __restrict__ qkv, const float* __restrict__ part, int rows, int Mp, int nq, int nkv,
-    int d, KvDev kv, RopeTab tab) {
+    int d, ChunkList chunks, DecDev dec, RopeFreq freq, KvDev kv) {
   const int r = blockIdx.x;
+  const int tid = threadIdx.x;
   const int h0 = blockIdx.y * kRopeHeads;
   const int nh = nq + 2 * nkv;
   const int ld = nh * d;
@@ -358,76 +281,88 @@ __global__ __launch_bounds__(64) void rope_append_wide_kernel(
   bf16* row = qkv + (size_t)r * ld;
   const int hend = min(h0 + kRopeHeads, nh);
   if (r >= rows) {
-    for (int c = h0 * d + threadIdx.x * 8; c < hend * d; c += 64 * 8)
+    for (int c = h0 * d + tid * 8; c < hend * d; c += kRopeThreads * 8)
       *reinterpret_cast<u32x4*>(row + c) = u32x4{0, 0, 0, 0};
     return;
   }
   const float* pr = part ? part + (size_t)r * ld : nullptr;
   const size_t plane = (size_t)Mp * ld;
-  const int slot = tab.slot[r];
+  const int qk_groups = half / 8;  // 8-pair items per q / k head
+  const int v_groups = d / 8;      // 8-value items per v head
+  // the workgroup's q / k heads come first, then its v heads
+  const int qk_end = min(hend, nq + nkv);
+  const int n_qk = max(qk_end - h0, 0) * qk_groups;
+  const int v_begin = max(h0, nq + nkv);
+  const int items = n_qk + max(hend - v_begin, 0) * v_groups;
+  // one item per thread (d <= 128: at most 16 heads x 16 items)
+  const int it = tid;
+  const bool has = it < items;
+  const bool is_qk = it < n_qk;
+  const int h = is_qk ? h0 + it / qk_groups : v_begin + (it - n_qk) / v_groups;
+  const int t = is_qk ? it % qk_groups : (it - n_qk) % v_groups;
+  u32x4 av{0, 0, 0, 0}, bv{0, 0, 0, 0};
+  if (has) {
+    if (is_qk) {
+      av = row8<SPLITS>(row, pr, plane, h * d + t * 8);
+      bv = row8<SPLITS>(row, pr, plane, h * d + t * 8 + half);
+    } else {
+      av = row8<SPLITS>(row, pr, plane, h * d + t * 8);
+    }
+  }
+  int pos, slot;
+  row_pos_slot(chunks, dec, kv.page_size, kv.num_pages, r, &pos, &slot);
   const int page = slot >= 0 ? slot / kv.page_size : -1;
   const int off = slot >= 0 ? slot % kv.page_size : 0;
-  const float* cs = tab.cs + (size_t)r * half;
-  const float* sn = tab.sn + (size_t)r * half;
-  const int qk_groups = half / 8;  // 8-pair groups per q / k head
-  const int v_groups = d / 8;      // 8-value groups per v head
-  // items: (head, group) over the workgroup's heads, in head order
-  int items = 0;
-  for (int h = h0; h < hend; ++h) items += h >= nq + nkv ? v_groups : qk_groups;
-  for (int it = threadIdx.x; it < items; it += 64) {
-    int h = h0, t = it;
-    while (true) {  // at most 4 heads
-      const int per = h >= nq + nkv ? v_groups : qk_groups;
-      if (t < per) break;
-      t -= per;
-      ++h;
+  __shared__ float cs_tab[kRopeMaxPairs], sn_tab[kRopeMaxPairs];
+  if (n_qk > 0) {  // uniform
+    if (tid < half) rope_cos_sin(pos, freq.inv[tid], &cs_tab[tid], &sn_tab[tid]);
+    __syncthreads();
+  }
+  if (!has) return;
+  bf16* u = row + h * d;
+  if (is_qk) {
+    const int i0 = t * 8;
+    u32x4 oa, ob;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = __uint_as_float(av[e] << 16), a1 = __uint_as_float(av[e] & 0xffff0000u);
+      const float b0 = __uint_as_float(bv[e] << 16), b1 = __uint_as_float(bv[e] & 0xffff0000u);
+      const float c0 = cs_tab[i0 + 2 * e], c1 = cs_tab[i0 + 2 * e + 1];
+      const float s0 = sn_tab[i0 + 2 * e], s1 = sn_tab[i0 + 2 * e + 1];
+      oa[e] = pack2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+      ob[e] = pack2(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
     }
-    bf16* u = row + h * d;
-    if (h < nq + nkv) {
-      const int i0 = t * 8;
-      const u32x4 av = row8<SPLITS>(row, pr, plane, h * d + i0);
-      const u32x4 bv = row8<SPLITS>(row, pr, plane, h * d + i0 + half);
-      u32x4 oa, ob;
+    *reinterpret_cast<u32x4*>(u + i0) = oa;
+    *reinterpret_cast<u32x4*>(u + i0 + half) = ob;
+    if (h >= nq && page >= 0) {
+      bf16* kp = kv.k_page(page, h - nq) + (size_t)off * d;
+      *reinterpret_cast<u32x4*>(kp + i0) = oa;
+      *reinterpret_cast<u32x4*>(kp + i0 + half) = ob;
+    }
+  } else {
+    const int gv = h - nq - nkv, dd = t * 8;
+    if (pr) *reinterpret_cast<u32x4*>(u + dd) = av;
+    if (page < 0) return;
+    bf16* vp = kv.v_page(page, gv) + (size_t)dd * kv.page_size + off;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a0 = __uint_as_float(av[e] << 16), a1 = __uint_as_float(av[e] & 0xffff0000u);
-        const float b0 = __uint_as_float(bv[e] << 16), b1 = __uint_as_float(bv[e] & 0xffff0000u);
-        const float c0 = cs[i0 + 2 * e], c1 = cs[i0 + 2 * e + 1];
-        const float s0 = sn[i0 + 2 * e], s1 = sn[i0 + 2 * e + 1];
-        oa[e] = pack2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-        ob[e] = pack2(a0 * s0 + b0 * c0, a1 * s1 + b1 * c1);
-      }
-      *reinterpret_cast<u32x4*>(u + i0) = oa;
-      *reinterpret_cast<u32x4*>(u + i0 + half) = ob;
-      if (h >= nq && page >= 0) {
-        bf16* kp = kv.k_page(page, h - nq) + (size_t)off * d;
-        *reinterpret_cast<u32x4*>(kp + i0) = oa;
-        *reinterpret_cast<u32x4*>(kp + i0 + half) = ob;
-      }
-    } else {
-      const int gv = h - nq - nkv, dd = t * 8;
-      const u32x4 vv = row8<SPLITS>(row, pr, plane, h * d + dd);
-      if (pr) *reinterpret_cast<u32x4*>(u + dd) = vv;
-      if (page < 0) continue;
-      bf16* vp = kv.v_page(page, gv) + (size_t)dd * kv.page_size + off;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vp[(2 * j) * kv.page_size] = (bf16)(vv[j] & 0xffffu);
-        vp[(2 * j + 1) * kv.page_size] = (bf16)(vv[j] >> 16);
-      }
+    for (int j = 0; j < 4; ++j) {
+      vp[(2 * j) * kv.page_size] = (bf16)(av[j] & 0xffffu);
+      vp[(2 * j + 1) * kv.page_size] = (bf16)(av[j] >> 16);
     }
   }
 }
 
 hipError_t launch_rope_append_wide(bf16* qkv, const float* part, int splits, int rows, int Mp,
-                                   int nq, int nkv, int d, const KvDev& kv, const RopeTab& tab,
-                                   hipStream_t s) {
+                                   int nq, int nkv, int d, float theta, const ChunkList& chunks,
+                                   const DecDev& dec, const KvDev& kv, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (d / 2 > kRopeMaxPairs || kRopeHeads * (d / 8) > kRopeThreads) return hipErrorInvalidValue;
+  const RopeFreq freq = rope_freq(d, theta);
   const int nh = nq + 2 * nkv;
   const dim3 grid(part ? Mp : rows, (nh + kRopeHeads - 1) / kRopeHeads);
-#define HL_ROPE(S_)                                                                          \
-  hipLaunchKernelGGL(rope_append_wide_kernel<S_>, grid, dim3(64), 0, s, qkv, part, rows, Mp, nq, \
-                     nkv, d, kv, tab)
+#define HL_ROPE(S_)                                                                           \
+  hipLaunchKernelGGL(rope_append_wide_kernel<S_>, grid, dim3(kRopeThreads), 0, s, qkv, part, rows, \
+                     Mp, nq, nkv, d, chunks, dec, freq, kv)
   if (!part) HL_ROPE(0);
   else if (splits == 2) HL_ROPE(2);
   else if (splits == 4) HL_ROPE(4);

@@ -69,26 +69,37 @@ def _gemm_epilogue(name: str) -> Optional[int]:
 class SlotLabeler:
     """Labels the library's dispatches, one call after another."""
 
-    def __init__(self):
+    def __init__(self, chained: bool = False):
         self.last = -1  # slot index of the previous dispatch of this call
+        # calls with the cross-layer RMSNorm fusion: an RMSNorm right after an
+        # unsplit down projection is that call's next-layer norm, not the
+        # first RMSNorm of the next call
+        self.chained = chained
 
     def label(self, kernel_name: str) -> Optional[str]:
         n = _base_name(kernel_name)
         if not n.startswith("hl::"):
             return None
         idx = SLOTS.index
-        if "rmsnorm_rope_table" in n:
-            s = "rmsnorm1"
-        elif "rmsnorm_kernel" in n:
-            # the second RMSNorm runs as a plain kernel when the O projection
-            # was not split
-            s = "gemm_o_reduce_rmsnorm2" if self.last == idx("gemm_o") else "rmsnorm1"
+        if "rmsnorm_kernel" in n:
+            # the first RMSNorm; the second one when the O projection was not
+            # split; the next layer's one after an unsplit down projection
+            # (cross-layer fusion)
+            if self.last == idx("gemm_o"):
+                s = "gemm_o_reduce_rmsnorm2"
+            elif self.last == idx("gemm_down") and self.chained:
+                s = "gemm_down_reduce"
+            else:
+                s = "rmsnorm1"
         elif "gemm_splitk_reduce_swiglu" in n:
             s = "gemm_gate_up_reduce"
         elif "gemm_splitk_reduce_norm" in n:
-            s = "gemm_o_reduce_rmsnorm2"
+            # after the down projection it also forms the next layer's RMSNorm
+            s = "gemm_down_reduce" if self.last == idx("gemm_down") else "gemm_o_reduce_rmsnorm2"
         elif re.search(r"gemm_splitk_reduce<1[,>]", n):  # <EPI_RESIDUAL[, splits]>
             s = "gemm_down_reduce"
+        elif "gemm_swiglu_agpr" in n:
+            s = "gemm_gate_up"
         elif "rope_append_wide" in n or "rope_kv_append" in n:
             s = "rope_kv_append"
         elif "attention_merge" in n:
@@ -129,7 +140,16 @@ def kernel_durations(trace_csv: str, skip: int = 0) -> Dict[str, List[float]]:
         s = lab.label(r["Kernel_Name"])
         if s:
             out[s].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
-    return {k: v[skip:] if len(v) > skip else v for k, v in out.items()}
+    return _drop_setup({k: v[skip:] if len(v) > skip else v for k, v in out.items()})
+
+
+def _drop_setup(per_slot: Dict[str, List[float]]) -> Dict[str, List[float]]:
+    """Leave out slots dispatched in fewer than a tenth of the calls: set-up
+    work of the profiled program, such as the one RMSNorm that forms the
+    first normalised input of the chained (layer-stack) call, whose own first
+    RMSNorm slot is empty."""
+    most = max((len(v) for v in per_slot.values()), default=0)
+    return {k: v for k, v in per_slot.items() if 10 * len(v) >= most}
 
 
 def counter_values(counter_csv: str, counter: str) -> Tuple[Dict[str, List[float]], float]:
@@ -151,7 +171,7 @@ def counter_values(counter_csv: str, counter: str) -> Tuple[Dict[str, List[float
         s = lab.label(r["Kernel_Name"])
         if s:
             out[s].append(v)
-    return out, calib
+    return _drop_setup(out), calib
 
 
 def _mean(v: Iterable[float]) -> float:

@@ -70,7 +70,7 @@ class Stage:
 
 def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ffn: int,
                  chunk_lens: Sequence[int], chunk_starts: Sequence[int],
-                 ctx_lens: Sequence[int], pad: int = 16) -> List[Stage]:
+                 ctx_lens: Sequence[int], pad: int = 16, chained: bool = False) -> List[Stage]:
     """Algorithmic flops and bytes of every kernel slot of one layer call, in
     the library's launch order and under its slot names.
 
@@ -79,7 +79,11 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     out, residual in); a split-K reduce carries only what its fused epilogue
     adds to the algorithm (the second RMSNorm's output and gain), so a plain
     reduce and the attention key-split merge carry none -- their time is
-    overhead of the launch shape, not work of the layer."""
+    overhead of the launch shape, not work of the layer.
+
+    ``chained``: the call with the cross-layer RMSNorm fusion, whose first
+    RMSNorm was formed by the previous layer and whose down-projection reduce
+    forms the next layer's (the same work, one slot later)."""
     H, nq, nkv, d, F = hidden, n_q_heads, n_kv_heads, head_dim, ffn
     Lp = int(sum(chunk_lens))
     Bd = len(ctx_lens)
@@ -88,7 +92,8 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     nqkv = (nq + 2 * nkv) * d
     kvB = 2 * nkv * d * 2
     st: List[Stage] = []
-    st.append(Stage("rmsnorm1", 3 * M * H, 2 * M * H * 2 + H * 2))
+    norm1 = (3 * M * H, 2 * M * H * 2 + H * 2)
+    st.append(Stage("rmsnorm1", *((0.0, 0.0) if chained else norm1)))
     st.append(Stage("gemm_qkv", 2 * Mp * H * nqkv, H * nqkv * 2 + M * H * 2 + M * nqkv * 2))
     # RoPE + KV append (it also sums the QKV split-K partials: not algorithmic)
     st.append(Stage("rope_kv_append", 6 * M * (nq + nkv) * d,
@@ -111,7 +116,9 @@ def layer_stages(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ff
     st.append(Stage("gemm_gate_up", 2 * Mp * H * 2 * F, 2 * F * H * 2 + M * H * 2 + M * F * 2))
     st.append(Stage("gemm_gate_up_reduce", 0.0, 0.0))
     st.append(Stage("gemm_down", 2 * Mp * F * H, F * H * 2 + M * F * 2 + 2 * M * H * 2))
-    st.append(Stage("gemm_down_reduce", 0.0, 0.0))
+    # chained: the next layer's RMSNorm of out inside the reduce (xn_next out
+    # and the gain; out itself is the down projection's)
+    st.append(Stage("gemm_down_reduce", *((3 * M * H, M * H * 2 + H * 2) if chained else (0.0, 0.0))))
     for s in st:
         s.bound = "mfma" if s.t_math() > s.t_mem() else "hbm"
     return st

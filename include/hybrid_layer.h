@@ -61,8 +61,9 @@ extern "C" {
 
 typedef uint16_t hl_bf16;
 
-/* Layer shape.  hidden, ffn and n_q_heads*head_dim must be multiples of 64;
- * n_q_heads a multiple of n_kv_heads; head_dim 64 or 128; page_size 16. */
+/* Layer shape.  hidden, ffn and n_q_heads*head_dim must be multiples of 64,
+ * hidden at most 16384 (HL_ERR_UNSUPPORTED); n_q_heads a multiple of
+ * n_kv_heads; head_dim 64 or 128; page_size 16. */
 typedef struct {
   int32_t hidden, n_q_heads, n_kv_heads, head_dim, ffn, page_size;
   float rms_eps;    /* added to mean(x^2) inside the square root */
@@ -171,6 +172,38 @@ int hl_layer_forward_timed(const hl_config* cfg, const hl_weights* w, const hl_b
                            const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
                            const hl_taps* taps, hipEvent_t* stage_events, hipStream_t stream);
 const char* hl_stage_name(int stage);
+
+/* Cross-layer fusion of the first RMSNorm.  In a stack of layers the input
+ * of layer l + 1 is the output of layer l, which the results of a layer are
+ * written for (preallocated contiguous memory handed to the next layer:
+ * gitcode.csdn.net SARATHI summary, part 2 item 3).  Layer l's last kernel,
+ * the split-K reduce of the down projection, holds whole output rows, so it
+ * can also store layer l + 1's normalised input, and layer l + 1 skips its
+ * own RMSNorm launch.  Fields (device pointers, each may be NULL):
+ *   xn_in   [Mp, H]: RMSNorm(x) * g_attn of THIS layer with eps =
+ *           cfg->rms_eps and pad rows zero, as the previous call's xn_next
+ *           left it (not checked).  When set, the layer's own RMSNorm is not
+ *           run (its stage slot times empty) and taps->xn1 is not written.
+ *   g_next  [H]: gain of the RMSNorm applied to this layer's output (the
+ *           next layer's g_attn, or the model's final norm).
+ *   xn_next [Mp, H]: receives RMSNorm(out) * g_next with eps =
+ *           cfg->rms_eps, pad rows zero; required when g_next is set and
+ *           must alias none of x, out, xn_in (HL_ERR_SHAPE).
+ * Mp = M rounded up to `pad`, as for the taps. */
+typedef struct {
+  const hl_bf16* xn_in;
+  const hl_bf16* g_next;
+  hl_bf16* xn_next;
+} hl_chain;
+
+/* hl_layer_forward with the cross-layer RMSNorm fusion above (chain NULL:
+ * the same as hl_layer_forward) and, when stage_events is not NULL, the stage
+ * events of hl_layer_forward_timed.  Workspace as for hl_layer_forward. */
+int hl_layer_forward_chain(const hl_config* cfg, const hl_weights* w, const hl_bf16* x,
+                           const hl_chunk* chunks, int32_t n_chunks, const hl_decodes* dec,
+                           const hl_kv* kv, hl_bf16* out, void* ws, size_t ws_bytes, int32_t pad,
+                           const hl_taps* taps, const hl_chain* chain, hipEvent_t* stage_events,
+                           hipStream_t stream);
 
 /* hl_layer_forward without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

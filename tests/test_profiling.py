@@ -3,7 +3,7 @@ from chunked_prefill_hybrid_rmsnorm_amd.profiling import SLOTS, SlotLabeler
 
 GEMM = "void hl::gemm_dma_kernel<288, 128, 2, 4, {e}, 3, 64>(unsigned short const*, int)"
 SPLIT_CALL = [
-    "void hl::rmsnorm_rope_table_kernel<8>(unsigned short const*)",
+    "void hl::rmsnorm_kernel<8>(unsigned short const*)",
     GEMM.format(e=0),
     "void hl::rope_append_wide_kernel<4>(unsigned short*, float const*)",
     "void hl::attention_kernel<128>(hl::AttnArgs)",
@@ -65,3 +65,21 @@ def test_mfma_summary_from_counter_rows(tmp_path):
     assert e["flops"] == 1000.0 * 512
     assert e["active_cycles_per_xcd"] == 2.0 and XCDS == 8
     assert abs(e["mfma_util"] - 500.0 / (SIMDS * 2.0)) < 1e-12
+
+
+def test_chained_call_labels():
+    """Cross-layer fusion: no first RMSNorm, the down reduce also normalises;
+    unsplit, the next layer's RMSNorm follows the down projection."""
+    lab = SlotLabeler()
+    chained = SPLIT_CALL[1:10] + ["void hl::gemm_splitk_reduce_norm<4, 4>(float const*)"]
+    assert [lab.label(k) for k in chained] == list(SLOTS[1:])
+    lab = SlotLabeler(chained=True)
+    got = [lab.label(k) for k in PLAIN_CALL[1:] + ["void hl::rmsnorm_kernel<8>(unsigned short const*)"]]
+    assert got[-2:] == ["gemm_down", "gemm_down_reduce"]
+
+
+def test_agpr_swiglu_kernel_is_the_gate_up_slot():
+    lab = SlotLabeler()
+    lab.label(GEMM.format(e=1))
+    assert lab.label("void hl::gemm_swiglu_agpr_kernel<288>(unsigned short const*)") == "gemm_gate_up"
+    assert lab.label(GEMM.format(e=1)) == "gemm_down"
