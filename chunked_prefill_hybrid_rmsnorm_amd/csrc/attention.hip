@@ -24,6 +24,7 @@
 // A decode that falls inside one slice is finished by its wave; otherwise
 // each slice leaves a partial result for the merge.
 #include <atomic>
+#include <type_traits>
 #include <string.h>
 
 #include "attn_common.h"
@@ -112,7 +113,7 @@ __device__ __forceinline__ void prefill_copy(char* stage, const KvDev& kv, int g
 }
 
 template <int D>
-__device__ __forceinline__ void prefill_frags(KvFrag<D>& f, const char* stage, int l16, int q) {
+__device__ __forceinline__ void prefill_frags_k(KvFrag<D>& f, const char* stage, int l16, int q) {
   constexpr int PAGE = PfStage<D>::PAGE;
 #pragma unroll
   for (int hp = 0; hp < 2; ++hp) {
@@ -122,12 +123,23 @@ __device__ __forceinline__ void prefill_frags(KvFrag<D>& f, const char* stage, i
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) f.k[hp][ks] = ld16(kr + (((ks * 4 + q) ^ k_swz(row)) * 16));
   }
+}
+
+template <int D>
+__device__ __forceinline__ void prefill_frags_v(KvFrag<D>& f, const char* stage, int l16, int q) {
+  constexpr int PAGE = PfStage<D>::PAGE;
   const char* vb = stage + (2 + (q >> 1)) * PAGE;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
     const int dim = db * 16 + l16;
     f.v[db] = ld16(vb + dim * 32 + (((q & 1) ^ v_swz(dim)) * 16));
   }
+}
+
+template <int D>
+__device__ __forceinline__ void prefill_frags(KvFrag<D>& f, const char* stage, int l16, int q) {
+  prefill_frags_k<D>(f, stage, l16, q);
+  prefill_frags_v<D>(f, stage, l16, q);
 }
 
 // Merge the (m, l, o) of the same rows over another key range into `a`
@@ -230,29 +242,41 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   init_acc<D>(a[0]);
   init_acc<D>(a[1]);
   const float scale = kAttnLog2e * rsqrtf((float)D);
-  static_assert(kPfStages == 3, "the waits below count one step in flight behind the current");
-  if (my_n > 0) issue(0);
-  if (my_n > 1) issue(1);
+  static_assert(kPfStages >= 3 && kPfStages <= 4, "the waits below allow 0 .. 2 steps in flight");
+  for (int s = 0; s + 1 < kPfStages; ++s)
+    if (s < my_n) issue(s);
   // the group's own steps (the same loop shape as a single group, so that
   // `busy`, invariant, can take the whole loop apart), then a barrier for
-  // each step the other group has beyond them (at most one)
-  int i = 0;
-  for (; i < my_n; ++i) {
-    // this step's copies have landed (the next step's may still be in flight)
-    if (i + 1 < my_n)
+  // each step the other group has beyond them (at most one).  Every step but
+  // the group's last ends below k1 <= v_end, so only the last one (peeled
+  // off the loop: one copy of the step code in the loop keeps the register
+  // budget) may have V to mask.
+  auto step = [&](int i, auto last) {
+    // this step's copies have landed; those of up to kPfStages - 2 later
+    // steps may still be in flight
+    const int ahead = min(kPfStages - 2, my_n - 1 - i);
+    if (ahead >= 2)
+      wait_vmcnt<2 * PfStage<D>::PER_WAVE>();
+    else if (ahead == 1)
       wait_vmcnt<PfStage<D>::PER_WAVE>();
     else
       wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (i + 2 < my_n) issue(i + 2);
-    if (!busy) continue;
+    // into the slot of step i - 1, which every wave finished reading before
+    // this barrier
+    if (i + kPfStages - 1 < my_n) issue(i + kPfStages - 1);
+    if (!busy) return;
     KvFrag<D> f;
     prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
     const int t0 = kg0 + i * 32;
-    compute_step<D, 2>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale, q);
-  }
+    compute_step<D, 2, decltype(last)::value>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale,
+                                              q);
+  };
+  int i = 0;
+  for (; i + 1 < my_n; ++i) step(i, std::false_type{});
+  if (my_n > 0) step(i++, std::true_type{});
   for (; i < n_iter; ++i) __builtin_amdgcn_s_barrier();
   // group 1 hands its rows' (m, l, o) to group 0 through the rings' LDS:
   // per wave and row block, D/4 + 2 floats per lane, lane-minor
@@ -398,8 +422,11 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int lan
   }
 }
 
+// Register budget: two waves per SIMD in either shape (the four-wave
+// workgroups ask for two resident workgroups per CU), so that a SIMD can
+// interleave a second wave's MFMAs, softmax or loads with the first's
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs A) {
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attention_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(1024)))
   char ring[NW / kPfHalfWaves * kPfStages * PfStage<D>::BYTES];
   // the wave index is uniform across the wave: keep it (and everything derived

@@ -95,22 +95,18 @@ constexpr float kRescaleSlack = 8.f;
 // valid V (past the request, or a stand-in page) and are zeroed before the
 // product.  `lim_min[rb]` is the smallest row_limit over the wave's rows of
 // block rb: a step below it and below v_end needs no masking at all.
+//
+// The step runs in three phases, which the ping-pong prefill loop places in
+// different halves of its schedule: the scores (MFMA), the online softmax
+// (VALU), and the probability-weighted V sum (MFMA).
+//
+// VMASK = false: the caller knows every key of the step is below v_end (all
+// steps but a segment's last), so no V mask is formed.  The mask is a
+// compile-time choice because the compiler turns a runtime test of it into
+// selects on every V register of every step.
 template <int D, int NRB>
-__device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<D>& f,
-                                             const bf16x8 (&qf)[NRB][D / 32], int t0,
-                                             const int (&row_limit)[NRB],
-                                             const int (&lim_min)[NRB], int k_end, int v_end,
-                                             float scale, int q) {
-  const bool v_full = t0 + 31 < v_end;
-  uint32_t vm[4];  // keep-masks of this lane's V keys t0 + 8q + 2w, + 1
-  if (!v_full) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int t = t0 + 8 * q + 2 * w;
-      vm[w] = (t < v_end ? 0x0000ffffu : 0u) | (t + 1 < v_end ? 0xffff0000u : 0u);
-    }
-  }
-  f32x4 s[NRB][2];
+__device__ __forceinline__ void step_scores(f32x4 (&s)[NRB][2], const KvFrag<D>& f,
+                                            const bf16x8 (&qf)[NRB][D / 32]) {
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -120,6 +116,34 @@ __device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<
       for (int ks = 0; ks < D / 32; ++ks)
         s[rb][hp] = mfma16x16x32(as_bf16x8(f.k[hp][ks]), qf[rb][ks], s[rb][hp]);
     }
+}
+
+// Zero V of the step's keys at or past v_end (a request's last page read
+// past its end, or a stand-in page), whose probabilities are 0 but whose
+// bytes are arbitrary.  Wave-uniform test.
+template <int D>
+__device__ __forceinline__ void mask_v_tail(KvFrag<D>& f, int t0, int v_end, int q) {
+  if (t0 + 31 < v_end) return;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // keep-masks of this lane's V keys t0 + 8q + 2w, + 1
+    const int t = t0 + 8 * q + 2 * w;
+    const uint32_t vm = (t < v_end ? 0x0000ffffu : 0u) | (t + 1 < v_end ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) f.v[db][w] &= vm;
+  }
+}
+
+// Online softmax of one step: masks the scores of keys a row may not see,
+// moves the running max (rescaling o and l), adds the step's probabilities to
+// l and packs them as the B operand of the V product.  With VMASK, V of keys
+// at or past v_end is zeroed in place.
+template <int D, int NRB, bool VMASK>
+__device__ __forceinline__ void step_softmax(AttnAcc<D> (&a)[NRB], f32x4 (&s)[NRB][2],
+                                             KvFrag<D>& f, bf16x8 (&pf)[NRB], int t0,
+                                             const int (&row_limit)[NRB],
+                                             const int (&lim_min)[NRB], int k_end, int v_end,
+                                             float scale, int q) {
+  if (VMASK) mask_v_tail<D>(f, t0, v_end, q);
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     AttnAcc<D>& acc = a[rb];
@@ -171,17 +195,32 @@ __device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<
       pk[hp * 2 + 1] = pack2(p[2], p[3]);
     }
     acc.l += psum;
-    const bf16x8 pf = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      u32x4 va = f.v[db];
-      if (!v_full) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) va[w] &= vm[w];
-      }
-      acc.o[db] = mfma16x16x32(as_bf16x8(va), pf, acc.o[db]);
-    }
+    pf[rb] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
   }
+}
+
+template <int D, int NRB>
+__device__ __forceinline__ void step_pv(AttnAcc<D> (&a)[NRB], const KvFrag<D>& f,
+                                        const bf16x8 (&pf)[NRB]) {
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      a[rb].o[db] = mfma16x16x32(as_bf16x8(f.v[db]), pf[rb], a[rb].o[db]);
+}
+
+template <int D, int NRB, bool VMASK = true>
+__device__ __forceinline__ void compute_step(AttnAcc<D> (&a)[NRB], const KvFrag<D>& fin,
+                                             const bf16x8 (&qf)[NRB][D / 32], int t0,
+                                             const int (&row_limit)[NRB],
+                                             const int (&lim_min)[NRB], int k_end, int v_end,
+                                             float scale, int q) {
+  KvFrag<D> f = fin;
+  f32x4 s[NRB][2];
+  bf16x8 pf[NRB];
+  step_scores<D, NRB>(s, f, qf);
+  step_softmax<D, NRB, VMASK>(a, s, f, pf, t0, row_limit, lim_min, k_end, v_end, scale, q);
+  step_pv<D, NRB>(a, f, pf);
 }
 
 // Smallest value of v over the wave.
@@ -247,18 +286,19 @@ __device__ __forceinline__ void attend_segment(AttnAcc<D>& a, const bf16x8 (&qf)
   const int lm[1] = {wave_min(row_limit)};
   // keys from block blk_end on come from a stand-in page: zero their V
   const int v_end = min(kv_len, blk_end * 16);
+  // every step but the last ends below k1 <= v_end: only the last masks V
   KvFrag<D> fa, fb;
   load(fa, 0);
   int i = 0;
   for (; i + 2 < nst; i += 2) {
     load(fb, i + 1);
-    compute_step<D, 1>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
+    compute_step<D, 1, false>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
     load(fa, i + 2);
-    compute_step<D, 1>(ab, fb, qb, k0 + 32 * (i + 1), rl, lm, k1, v_end, scale, q);
+    compute_step<D, 1, false>(ab, fb, qb, k0 + 32 * (i + 1), rl, lm, k1, v_end, scale, q);
   }
   if (i + 1 < nst) {  // two steps left, the first already loaded
     load(fb, i + 1);
-    compute_step<D, 1>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
+    compute_step<D, 1, false>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
     compute_step<D, 1>(ab, fb, qb, k0 + 32 * (i + 1), rl, lm, k1, v_end, scale, q);
   } else {
     compute_step<D, 1>(ab, fa, qb, k0 + 32 * i, rl, lm, k1, v_end, scale, q);
