@@ -179,6 +179,7 @@ struct Choice {
   int splits;  // K splits (1 = none)
   int wide;    // 1: 256-weight-row tile, two stages (two or more row tiles, long k loops)
   int agpr;    // 1: SwiGLU on the one-wave-per-SIMD kernel (gemm_agpr.hip)
+  int agpr_fn; // > 0: plain / residual GEMM on the one-wave-per-SIMD kernel, 32 agpr_fn columns
 };
 
 // Split K (powers of two, at most 8, at least 8 k-steps per split) while the
@@ -203,6 +204,7 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   const int ksteps = k / kGemmBK;
   c.wide = 0;
   c.agpr = 0;
+  c.agpr_fn = 0;
   if (c.big && mt >= 2 && epi == EPI_SWIGLU && ksteps >= 16) {
     // one wave per SIMD, 112 outputs per tile, no K split: taken where its
     // rounds of 256 workgroups are at least as full as the default tile's
@@ -236,6 +238,27 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
       c.wide = 1;
       c.splits = sp;
       return c;
+    }
+  }
+  if (c.big && mt >= 2 && epi != EPI_SWIGLU && ksteps >= 32) {
+    // one wave per SIMD with AGPR accumulators, where the wide tile above
+    // does not apply (plain GEMMs; k loops too short for it): the widest
+    // tile whose workgroups, K split to fill the CUs, take at least 240 of
+    // the 256 CUs in one round.  Llama-2-70B-shaped QKV: 160 columns, 2 x 64
+    // tiles x 2 splits, 112.4 -> 84.2 us (+4 us for the RoPE step to sum the
+    // partials); O: 128 columns, 75.5 -> 71.4 us.  Residual GEMMs with long
+    // k loops keep the other tiles: the Llama-2-70B-shaped down projection
+    // (448 k-steps) took 274 us here against 213 on the wide tile, and the
+    // 512-row Mistral-shaped one (224 k-steps) 68.1 against 62.6 us.
+    for (int fn : {7, 5, 4}) {
+      if (epi == EPI_RESIDUAL && (fn == 7 || ksteps > 128)) continue;  // fn 7: epilogue spills
+      const int tiles = mt * ((n + 32 * fn - 1) / (32 * fn));
+      const int sp = splits_for(tiles, ksteps);
+      if (tiles * sp >= 240 && tiles * sp <= 256) {
+        c.agpr_fn = fn;
+        c.splits = sp;
+        return c;
+      }
     }
   }
   if (epi == EPI_SWIGLU) {
@@ -311,6 +334,11 @@ template <int EPI>
 static hipError_t run_choice(const Choice& ch, const bf16* a, const bf16* w, const bf16* w2,
                              bf16* c, const bf16* r, float* part, int m, int mp, int n, int k,
                              hipStream_t s) {
+  if constexpr (EPI != EPI_SWIGLU) {
+    if (ch.agpr_fn)
+      return launch_gemm_agpr(static_cast<GemmEpilogue>(EPI), ch.agpr_fn, a, w, c, r, part, m, mp,
+                              n, k, ch.splits, ch.r256, s);
+  }
   if (ch.big && ch.r256) return run_big<EPI, 256>(ch, a, w, w2, c, r, part, m, mp, n, k, s);
   if (ch.big) return run_big<EPI, 288>(ch, a, w, w2, c, r, part, m, mp, n, k, s);
   // small batches (decode-heavy iterations): the row tile shrinks with the

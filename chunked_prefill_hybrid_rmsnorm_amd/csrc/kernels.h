@@ -30,6 +30,12 @@ size_t gemm_workspace_bytes(GemmEpilogue epi, int m_padded, int n, int k);
 // of 112 outputs, no K split.
 hipError_t launch_swiglu_agpr(const bf16* a, const bf16* wg, const bf16* wu, bf16* act, int mp,
                               int f, int k, bool rows256, hipStream_t s);
+// One-wave-per-SIMD plain / residual GEMM (gemm_agpr.hip): BM = 288 (or 256
+// with rows256) x 32 fn weight rows per tile, fn in {4, 5, 7}; with splits > 1
+// it writes fp32 partials [splits][mp][n] to `part` instead of c.
+hipError_t launch_gemm_agpr(GemmEpilogue epi, int fn, const bf16* a, const bf16* w, bf16* c,
+                            const bf16* r, float* part, int m, int mp, int n, int k, int splits,
+                            bool rows256, hipStream_t s);
 hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf16* w2, bf16* c,
                        const bf16* residual, void* ws, int m, int m_padded, int n, int k,
                        hipStream_t s, hipEvent_t mid = nullptr);
