@@ -60,10 +60,16 @@ def _base_name(name: str) -> str:
 
 
 def _gemm_epilogue(name: str) -> Optional[int]:
+    """Epilogue template argument of a GEMM kernel name (0 store, 1 residual,
+    2 SwiGLU): the fifth of gemm_dma_kernel<...>, the third of
+    gemm_agpr_kernel<...>."""
     m = re.search(r"gemm_dma_kernel<([^>]*)>", name)
-    if not m:
-        return None
-    return int(m.group(1).split(",")[4])
+    if m:
+        return int(m.group(1).split(",")[4])
+    m = re.search(r"gemm_agpr_kernel<([^>]*)>", name)
+    if m:
+        return int(m.group(1).split(",")[2])
+    return None
 
 
 class SlotLabeler:
@@ -106,7 +112,7 @@ class SlotLabeler:
             s = "attention_merge"
         elif "attention_kernel" in n:
             s = "attention"
-        elif "gemm_dma_kernel" in n:
+        elif "gemm_dma_kernel" in n or "gemm_agpr_kernel" in n:
             epi = _gemm_epilogue(kernel_name)
             if epi == 0:
                 s = "gemm_qkv"

@@ -83,3 +83,13 @@ def test_agpr_swiglu_kernel_is_the_gate_up_slot():
     lab.label(GEMM.format(e=1))
     assert lab.label("void hl::gemm_swiglu_agpr_kernel<288>(unsigned short const*)") == "gemm_gate_up"
     assert lab.label(GEMM.format(e=1)) == "gemm_down"
+
+
+def test_agpr_plain_and_residual_kernels_label_by_epilogue():
+    lab = SlotLabeler()
+    qkv = "void hl::gemm_agpr_kernel<288, 5, 0>(unsigned short const*, int)"
+    res = "void hl::gemm_agpr_kernel<288, 4, 1>(unsigned short const*, int)"
+    assert lab.label(qkv) == "gemm_qkv"
+    assert lab.label(res) == "gemm_o"
+    lab.label("void hl::gemm_swiglu_agpr_kernel<288>(unsigned short const*)")
+    assert lab.label(res) == "gemm_down"
