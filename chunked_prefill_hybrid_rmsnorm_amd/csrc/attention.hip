@@ -37,6 +37,7 @@ constexpr int kPfHalfWaves = 4;  // waves of one prefill group
 constexpr int kPfRowsPerWave = 32;                         // two 16-row MFMA blocks
 constexpr int kPrefillRows = kPfRowsPerWave * kPfHalfWaves;  // rows per prefill workgroup
 constexpr int kPfStages = 3;                             // LDS ring depth of prefill K/V
+constexpr bool kPfPipelined = true;  // prefill waves score the next step during this step's softmax
 constexpr int kDecMinSliceSteps = 4;   // fewest 32-key steps in a decode slice
 constexpr int kDecMaxWaves = 4096;     // decode waves of one launch, all kv heads
 
@@ -245,39 +246,109 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   static_assert(kPfStages >= 3 && kPfStages <= 4, "the waits below allow 0 .. 2 steps in flight");
   for (int s = 0; s + 1 < kPfStages; ++s)
     if (s < my_n) issue(s);
-  // the group's own steps (the same loop shape as a single group, so that
-  // `busy`, invariant, can take the whole loop apart), then a barrier for
-  // each step the other group has beyond them (at most one).  Every step but
-  // the group's last ends below k1 <= v_end, so only the last one (peeled
-  // off the loop: one copy of the step code in the loop keeps the register
-  // budget) may have V to mask.
-  auto step = [&](int i, auto last) {
-    // this step's copies have landed; those of up to kPfStages - 2 later
-    // steps may still be in flight
-    const int ahead = min(kPfStages - 2, my_n - 1 - i);
-    if (ahead >= 2)
-      wait_vmcnt<2 * PfStage<D>::PER_WAVE>();
-    else if (ahead == 1)
-      wait_vmcnt<PfStage<D>::PER_WAVE>();
-    else
-      wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // into the slot of step i - 1, which every wave finished reading before
-    // this barrier
-    if (i + kPfStages - 1 < my_n) issue(i + kPfStages - 1);
-    if (!busy) return;
-    KvFrag<D> f;
-    prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
-    const int t0 = kg0 + i * 32;
-    compute_step<D, 2, decltype(last)::value>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale,
-                                              q);
-  };
-  int i = 0;
-  for (; i + 1 < my_n; ++i) step(i, std::false_type{});
-  if (my_n > 0) step(i++, std::true_type{});
-  for (; i < n_iter; ++i) __builtin_amdgcn_s_barrier();
+  if constexpr (kPfPipelined) {
+    // Each wave runs one step ahead of its softmax: while step i's softmax
+    // (VALU) and V product run, step i+1's K fragments are read and its
+    // scores multiplied, so a wave keeps the matrix pipe and the vector ALU
+    // busy together instead of in turn.  Stage t is waited for, and its
+    // copies made visible by the barrier, before any of its fragments are
+    // read; the copies issued after that barrier refill the slot of stage
+    // t-1, whose reads (the previous iteration's) this wave has seen land.
+    // Every wave passes my_n barriers, then one per step the other group has
+    // beyond them.
+    auto open_stage = [&](int t) {
+      const int after = min(kPfStages - 2, my_n - 1 - t);  // later stages that may be in flight
+      if (after >= 2)
+        wait_vmcnt<2 * PfStage<D>::PER_WAVE>();
+      else if (after == 1)
+        wait_vmcnt<PfStage<D>::PER_WAVE>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + kPfStages - 1 < my_n) issue(t + kPfStages - 1);
+    };
+    KvFrag<D> fk, fv;  // K of the step being scored; V of the step being summed
+    f32x4 sc[2][2];    // scores of the step whose softmax is next
+    bf16x8 pf[2];
+    if (my_n > 0) {
+      open_stage(0);
+      if (busy) {
+        prefill_frags_k<D>(fk, ring, l16, q);
+        prefill_frags_v<D>(fv, ring, l16, q);
+        step_scores<D, 2>(sc, fk, qf);
+      }
+    }
+    for (int i = 0; i + 1 < my_n; ++i) {
+      open_stage(i + 1);
+      if (!busy) continue;
+      const char* st = ring + ((i + 1) % kPfStages) * PfStage<D>::BYTES;
+      prefill_frags_k<D>(fk, st, l16, q);
+      // step i's max and rescale while step i+1's K reads are in flight;
+      // every step but the group's last ends below k1 <= v_end
+      float m_use[2];
+      step_softmax_head<D, 2, false>(a, sc, fv, m_use, kg0 + i * 32, row_limit, lim_min, k1,
+                                     v_end, scale, q);
+      // step i+1's scores (MFMA) interleaved with step i's exponentials
+      // (VALU): one MFMA, then three vector instructions
+      f32x4 sn[2][2];
+      step_scores<D, 2>(sn, fk, qf);
+      step_softmax_tail<D, 2>(a, sc, m_use, pf, scale);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      }
+      step_pv<D, 2>(a, fv, pf);
+      prefill_frags_v<D>(fv, st, l16, q);  // step i+1
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) sc[rb][hp] = sn[rb][hp];
+    }
+    if (my_n > 0 && busy) {  // the group's last step, V tail masked
+      step_softmax<D, 2, true>(a, sc, fv, pf, kg0 + (my_n - 1) * 32, row_limit, lim_min, k1,
+                               v_end, scale, q);
+      step_pv<D, 2>(a, fv, pf);
+    }
+    for (int i = my_n; i < n_iter; ++i) __builtin_amdgcn_s_barrier();
+  } else {
+    // the group's own steps (the same loop shape as a single group, so that
+    // `busy`, invariant, can take the whole loop apart), then a barrier for
+    // each step the other group has beyond them (at most one).  Every step but
+    // the group's last ends below k1 <= v_end, so only the last one (peeled
+    // off the loop: one copy of the step code in the loop keeps the register
+    // budget) may have V to mask.
+    auto step = [&](int i, auto last) {
+      // this step's copies have landed; those of up to kPfStages - 2 later
+      // steps may still be in flight
+      const int ahead = min(kPfStages - 2, my_n - 1 - i);
+      if (ahead >= 2)
+        wait_vmcnt<2 * PfStage<D>::PER_WAVE>();
+      else if (ahead == 1)
+        wait_vmcnt<PfStage<D>::PER_WAVE>();
+      else
+        wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // into the slot of step i - 1, which every wave finished reading before
+      // this barrier
+      if (i + kPfStages - 1 < my_n) issue(i + kPfStages - 1);
+      if (!busy) return;
+      KvFrag<D> f;
+      prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
+      const int t0 = kg0 + i * 32;
+      compute_step<D, 2, decltype(last)::value>(a, f, qf, t0, row_limit, lim_min, k1, v_end, scale,
+                                                q);
+    };
+    int i = 0;
+    for (; i + 1 < my_n; ++i) step(i, std::false_type{});
+    if (my_n > 0) step(i++, std::true_type{});
+    for (; i < n_iter; ++i) __builtin_amdgcn_s_barrier();
+  }
   // group 1 hands its rows' (m, l, o) to group 0 through the rings' LDS:
   // per wave and row block, D/4 + 2 floats per lane, lane-minor
   constexpr int XF = D / 4 + 2;

@@ -133,16 +133,18 @@ __device__ __forceinline__ void mask_v_tail(KvFrag<D>& f, int t0, int v_end, int
   }
 }
 
-// Online softmax of one step: masks the scores of keys a row may not see,
-// moves the running max (rescaling o and l), adds the step's probabilities to
-// l and packs them as the B operand of the V product.  With VMASK, V of keys
-// at or past v_end is zeroed in place.
+// Online softmax of one step, in two parts.  The head masks the scores of
+// keys a row may not see and moves the running max (rescaling o and l); it
+// returns the shift each row's exponents use.  The tail (straight-line
+// code, which a caller can interleave with independent MFMAs) forms the
+// step's probabilities, adds them to l and packs them as the B operand of
+// the V product.  With VMASK, V of keys at or past v_end is zeroed in place.
 template <int D, int NRB, bool VMASK>
-__device__ __forceinline__ void step_softmax(AttnAcc<D> (&a)[NRB], f32x4 (&s)[NRB][2],
-                                             KvFrag<D>& f, bf16x8 (&pf)[NRB], int t0,
-                                             const int (&row_limit)[NRB],
-                                             const int (&lim_min)[NRB], int k_end, int v_end,
-                                             float scale, int q) {
+__device__ __forceinline__ void step_softmax_head(AttnAcc<D> (&a)[NRB], f32x4 (&s)[NRB][2],
+                                                  KvFrag<D>& f, float (&m_use)[NRB], int t0,
+                                                  const int (&row_limit)[NRB],
+                                                  const int (&lim_min)[NRB], int k_end,
+                                                  int v_end, float scale, int q) {
   if (VMASK) mask_v_tail<D>(f, t0, v_end, q);
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -180,7 +182,16 @@ __device__ __forceinline__ void step_softmax(AttnAcc<D> (&a)[NRB], f32x4 (&s)[NR
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) acc.o[db] *= alpha;
     }
-    const float m_use = acc.m == -INFINITY ? 0.f : acc.m;
+    m_use[rb] = acc.m == -INFINITY ? 0.f : acc.m;
+  }
+}
+
+template <int D, int NRB>
+__device__ __forceinline__ void step_softmax_tail(AttnAcc<D> (&a)[NRB], const f32x4 (&s)[NRB][2],
+                                                  const float (&m_use)[NRB], bf16x8 (&pf)[NRB],
+                                                  float scale) {
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
     float psum = 0.f;
     uint32_t pk[4];
 #pragma unroll
@@ -188,15 +199,26 @@ __device__ __forceinline__ void step_softmax(AttnAcc<D> (&a)[NRB], f32x4 (&s)[NR
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(__builtin_fmaf(s[rb][hp][r], scale, -m_use));
+        p[r] = fast_exp2(__builtin_fmaf(s[rb][hp][r], scale, -m_use[rb]));
         psum += p[r];
       }
       pk[hp * 2 + 0] = pack2(p[0], p[1]);
       pk[hp * 2 + 1] = pack2(p[2], p[3]);
     }
-    acc.l += psum;
+    a[rb].l += psum;
     pf[rb] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
   }
+}
+
+template <int D, int NRB, bool VMASK>
+__device__ __forceinline__ void step_softmax(AttnAcc<D> (&a)[NRB], f32x4 (&s)[NRB][2],
+                                             KvFrag<D>& f, bf16x8 (&pf)[NRB], int t0,
+                                             const int (&row_limit)[NRB],
+                                             const int (&lim_min)[NRB], int k_end, int v_end,
+                                             float scale, int q) {
+  float m_use[NRB];
+  step_softmax_head<D, NRB, VMASK>(a, s, f, m_use, t0, row_limit, lim_min, k_end, v_end, scale, q);
+  step_softmax_tail<D, NRB>(a, s, m_use, pf, scale);
 }
 
 template <int D, int NRB>
