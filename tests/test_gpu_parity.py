@@ -85,7 +85,17 @@ def test_rmsnorm_step():
                                             (500, 512, 384, 1024, True),
                                             # 256-weight-row tiles with two stages (two row
                                             # tiles, long k loop): ragged rows, 4 K splits
-                                            (300, 304, 8192, 16384, True)])
+                                            (300, 304, 8192, 16384, True),
+                                            # one-wave-per-SIMD tiles: 160 columns (QKV-like),
+                                            # split in two and, without a workspace, unsplit
+                                            (560, 576, 10240, 8192, True),
+                                            (560, 576, 10240, 8192, False),
+                                            # 128 columns (O-like), plain and residual
+                                            (570, 576, 8192, 8192, True),
+                                            # 128 columns on 256-row tiles, 4 K splits
+                                            (500, 512, 4096, 4096, True),
+                                            # 224 columns (plain only)
+                                            (570, 576, 13440, 2048, True)])
 def test_gemm_step(m, mp, n, k, split):
     """Without a workspace K is not split (one launch, the long-k tile with two
     k-groups for the 288-row shapes); with one the partials are reduced."""
