@@ -123,6 +123,37 @@ def test_layer_forward_rejects_before_launch(lib):
              ctypes.byref(kv), fake + 4096, fake, 1 << 30, 16, None, None) == -1
 
 
+def test_layer_forward_chain_rejects_before_launch(lib):
+    """The stack-call fields are checked on the host before any launch (fake,
+    never-dereferenced pointers)."""
+    cfg = _cfg()
+    fake = 0x1000
+    w = B.hl_weights(*([fake] * 7))
+    kv = B.hl_kv(fake, 10)
+    ch = (B.hl_chunk * 1)(B.hl_chunk(4, 0, fake, 1))
+    dec = B.hl_decodes(0, None, None, 0, 0)
+    f = lib.hl_layer_forward_chain
+    x, out, ws = fake, fake + 4096, fake + 8192
+
+    def call(chain, events=None):
+        return f(ctypes.byref(cfg), ctypes.byref(w), x, ch, 1, ctypes.byref(dec), ctypes.byref(kv),
+                 out, ws, 1 << 30, 16, None, ctypes.byref(chain) if chain else None, events, None)
+
+    # g_next without xn_next
+    assert call(B.hl_chain(None, fake + 12288, None)) == -1
+    # xn_next aliasing out, x or xn_in
+    assert call(B.hl_chain(None, fake + 12288, out)) == -2
+    assert call(B.hl_chain(None, fake + 12288, x)) == -2
+    assert call(B.hl_chain(fake + 16384, fake + 12288, fake + 16384)) == -2
+    # a stage-event array with a missing event
+    events = (ctypes.c_void_p * (B.N_STAGES + 1))()
+    assert call(B.hl_chain(None, None, None), events) == -1
+    # hidden beyond what the row-wise RMSNorm kernels hold
+    big = B.hl_config(16384 + 64, 8, 8, 128, 1024, 16, 1e-5, 1e4)
+    assert f(ctypes.byref(big), ctypes.byref(w), x, ch, 1, ctypes.byref(dec), ctypes.byref(kv),
+             out, ws, 1 << 30, 16, None, None, None, None) == -3
+
+
 def test_gemm_entries_reject_before_launch(lib):
     """Shape errors and operands of 4 GiB or more come back before any launch
     (fake device pointers, no GPU needed)."""
