@@ -411,8 +411,15 @@ __device__ __forceinline__ int slice_begin(int s, const DecodeSplit& d) {
 __device__ __forceinline__ int slice_of(int t, const DecodeSplit& d) {
   return (int)(((long long)(t + 1) * d.P - 1) / d.S);
 }
-// S from the context lengths, and P = min(max_slices, S / kDecMinSliceSteps);
-// the attention waves and the merge compute it alike (one wave each)
+// P = min(max_slices, S / kDecMinSliceSteps) for S steps in all
+__device__ __forceinline__ DecodeSplit split_of(int S, int max_slices) {
+  DecodeSplit d;
+  d.S = S;
+  d.P = max(1, min(max_slices, S / kDecMinSliceSteps));
+  return d;
+}
+// S from the context lengths (one wave); the attention waves and the merge
+// compute it alike
 __device__ __forceinline__ DecodeSplit decode_split(const DecDev& dec, int max_slices, int lane) {
   int S = 0;
   for (int c0 = 0; c0 < dec.n; c0 += 64) {
@@ -420,10 +427,7 @@ __device__ __forceinline__ DecodeSplit decode_split(const DecDev& dec, int max_s
     const int st = j < dec.n ? decode_steps(dec.ctx_lens[j]) : 0;
     S += __builtin_amdgcn_readlane(wave_incl_scan(st, lane), 63);
   }
-  DecodeSplit d;
-  d.S = S;
-  d.P = max(1, min(max_slices, S / kDecMinSliceSteps));
-  return d;
+  return split_of(S, max_slices);
 }
 
 // Steps [t0, t1) of decode j (first step cj, nj steps) for kv head g; the
@@ -463,15 +467,22 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& A, const DecodeSpli
   }
 }
 
-// unit = s * nkv + g: the waves of a workgroup share slice s (same pages)
-template <int D>
-__device__ __forceinline__ void decode_wave(const AttnArgs& A, int unit, int lane, int l16,
-                                            int q) {
+// Work unit u = s * nkv + g (slice s, kv head g).  A workgroup's waves take
+// consecutive units, so they share slices (the same pages).  When the context
+// lengths give fewer slices than the grid has decode waves, every workgroup
+// takes fewer units, so the busy waves spread over all decode workgroups (and
+// compute units) instead of filling the first ones.
+template <int D, int NW>
+__device__ __forceinline__ void decode_wave(const AttnArgs& A, int wg, int wave, int lane,
+                                            int l16, int q) {
+  const DecodeSplit sp = decode_split(A.dec, A.dc_slices, lane);
+  const int units = sp.P * A.nkv;
+  const int per_wg = min(NW, (units + A.dc_wgs - 1) / A.dc_wgs);
+  if (wave >= per_wg) return;
+  const int unit = wg * per_wg + wave;
+  if (unit >= units) return;
   const int g = unit % A.nkv;
   const int s = unit / A.nkv;
-  if (s >= A.dc_slices) return;
-  const DecodeSplit sp = decode_split(A.dec, A.dc_slices, lane);
-  if (s >= sp.P) return;
   const int b0 = slice_begin(s, sp), b1 = slice_begin(s + 1, sp);
   int base = 0;  // steps of the decodes before this group of 64
   for (int c0 = 0; c0 < A.dec.n && base < b1; c0 += 64) {
@@ -515,53 +526,56 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attention_kernel(AttnArgs A) 
     const int per = A.pf_wgs / 8, rem = A.pf_wgs % 8, xcd = b % 8;
     prefill_block<D, NW>(A, xcd * per + min(xcd, rem) + b / 8, wave, lane, ring);
   } else
-    decode_wave<D>(A, (b - A.pf_wgs) * NW + wave, lane, l16, q);
+    decode_wave<D, NW>(A, b - A.pf_wgs, wave, lane, l16, q);
 }
 
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the parts of one
 // (row, head), stored consecutively from `base`; lane i takes dims D/64 i ...
-// Up to 16 parts are loaded in one round; more are loaded 8 at a time
+// Up to 32 parts: lane p loads the (m, l) of part p while every lane loads its
+// dims of all parts, in one round, and each part's weight is computed once,
+// by its lane, and read from there.  More parts are loaded 8 at a time
 // (indices clamped to the last part) in two passes.  Either way the parts are
-// summed in part order.
+// summed in part order with the same weights.
 template <int D>
 __device__ __forceinline__ void merge_unit(const float* __restrict__ o_part,
                                            const float* __restrict__ ml_part, size_t base,
                                            int n_parts, bf16* __restrict__ orow) {
   constexpr int PER = D / 64;
-  // up to 16 parts: every load in one round, then the sum from registers
-  // (n_parts is uniform over the block, so the guards are scalar branches)
-  constexpr int ONE = 16;
+  // n_parts is uniform over the block, so the guards are scalar branches
+  constexpr int ONE = 32;
+  const int lane = threadIdx.x;
   if (n_parts <= ONE) {
-    float mv[ONE], lv[ONE], ov[ONE][PER];
+    float mv = -INFINITY, lv = 0.f, ov[ONE][PER];
+    if (lane < n_parts) {
+      mv = ml_part[(base + lane) * 2];
+      lv = ml_part[(base + lane) * 2 + 1];
+    }
 #pragma unroll
     for (int u = 0; u < ONE; ++u) {
       if (u < n_parts) {
-        const size_t pi = base + u;
-        mv[u] = ml_part[pi * 2];
-        lv[u] = ml_part[pi * 2 + 1];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) ov[u][i] = o_part[pi * D + threadIdx.x * PER + i];
+        for (int i = 0; i < PER; ++i) ov[u][i] = o_part[(base + u) * D + lane * PER + i];
       }
     }
-    float mmax = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < ONE; ++u)
-      if (u < n_parts) mmax = fmaxf(mmax, mv[u]);
+    const float mmax = wave_max(mv);
+    const float wl = mv == -INFINITY ? 0.f : exp2f(mv - mmax);
     float o[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
     float lsum = 0.f;
 #pragma unroll
     for (int u = 0; u < ONE; ++u) {
-      if (u >= n_parts || mv[u] == -INFINITY) continue;  // no visible key in this part
-      const float w = exp2f(mv[u] - mmax);
-      lsum += w * lv[u];
+      if (u >= n_parts) continue;
+      // no visible key in this part
+      if (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), u)) == -INFINITY) continue;
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+      lsum += w * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), u));
 #pragma unroll
       for (int i = 0; i < PER; ++i) o[i] += w * ov[u][i];
     }
     const float inv = 1.f / lsum;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) orow[threadIdx.x * PER + i] = f2bf(o[i] * inv);
+    for (int i = 0; i < PER; ++i) orow[lane * PER + i] = f2bf(o[i] * inv);
     return;
   }
   constexpr int U = 8;
@@ -623,15 +637,22 @@ __global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs A) {
     const int j = r - A.chunks.n_rows;
     if (j >= A.dec.n) return;
     const int lane = threadIdx.x;
-    const DecodeSplit sp = decode_split(A.dec, A.dc_slices, lane);
-    int cj = 0;  // steps of the decodes before j
-    for (int c0 = 0; c0 < j; c0 += 64) {
+    // one pass over the context lengths: the steps of all decodes (the
+    // split), of the decodes before j (cj) and of decode j (nj)
+    int S = 0, cj = 0, nj = 0;
+    for (int c0 = 0; c0 < A.dec.n; c0 += 64) {
       const int i = c0 + lane;
-      const int st = i < j ? decode_steps(A.dec.ctx_lens[i]) : 0;
-      cj += __builtin_amdgcn_readlane(wave_incl_scan(st, lane), 63);
+      const int st = i < A.dec.n ? decode_steps(A.dec.ctx_lens[i]) : 0;
+      const int incl = wave_incl_scan(st, lane);
+      if (j >= c0 && j < c0 + 64) {
+        cj = S + __builtin_amdgcn_readlane(incl - st, j - c0);
+        nj = __builtin_amdgcn_readlane(st, j - c0);
+      }
+      S += __builtin_amdgcn_readlane(incl, 63);
     }
+    const DecodeSplit sp = split_of(S, A.dc_slices);
     const int s_lo = slice_of(cj, sp);
-    const int s_hi = slice_of(cj + decode_steps(A.dec.ctx_lens[j]) - 1, sp);
+    const int s_hi = slice_of(cj + nj - 1, sp);
     if (s_lo == s_hi) return;
     orow += (size_t)(A.dc_row0 + j) * A.nq * D + (size_t)h * D;
     merge_unit<D>(A.dc_o, A.dc_ml, (size_t)h * A.dc_pn + s_lo + j, s_hi - s_lo + 1, orow);
@@ -640,36 +661,54 @@ __global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs A) {
 
 // ---------------------------------------------------------------- host side
 // Prefill key split over workgroups: only when the chunk rows give few
-// workgroups, into segments of >= 256 keys (multiples of 32); each workgroup
-// splits its segment once more between its two wave groups.  Prefill alone
-// aims at ~256 workgroups, one per CU (split below 128).  Beside decodes it
-// aims at 64 (split below 64): there the decode waves set the kernel time,
-// every prefill workgroup takes a slot a decode wave group could use, and
-// every split adds partials for the merge to read.
+// workgroups, into segments of >= 256 keys (multiples of 32).  Prefill alone
+// aims at ~256 workgroups, one per CU (split below 128), each splitting its
+// segment once more between its two wave groups.  Beside decodes it aims at
+// 64 (split below 64): there the decode waves set the kernel time, every
+// prefill workgroup takes a slot a decode wave group could use, and every
+// split adds partials for the merge to read.
 constexpr int kPfAimAlone = 256, kPfAimHybrid = 64;
 // 128-row groups (over all kv heads) from which a chunk beside decodes runs
 // in four-wave workgroups
 constexpr int kPfFourWaveFrom = 256;
+// segment length of a chunk of few row groups over a long cached prefix
+constexpr int kPfFewSeg = 512;
+
+// prefill workgroups before any key split (128-row groups over all kv heads)
+// and the longest key range of the chunks
+static void chunk_extent(const ChunkList& chunks, int nq, int nkv, int* base, int* max_keys) {
+  const int G = nq / nkv;
+  *base = 0;
+  *max_keys = 0;
+  for (int i = 0; i < chunks.n; ++i) {
+    *base += (chunks.c[i].len * G + kPrefillRows - 1) / kPrefillRows * nkv;
+    *max_keys = max(*max_keys, chunks.c[i].start_pos + chunks.c[i].len);
+  }
+}
+
+// Beside decodes, a chunk of few row groups over a long cached prefix (a
+// tensor-parallel share: one or two kv heads) runs in four-wave workgroups
+// and walks its keys in segments of at most kPfFewSeg, up to ~256
+// workgroups, so that each CU holds one prefill and one decode workgroup:
+// Mistral-7B-shaped T=4 share 125.6 -> 120.6 us per layer; Llama-2-70B-shaped
+// T=8 share: attention 30.4 -> 28.8 us, its merge 7.8 -> 8.6 us (before:
+// eight-wave workgroups in 1024-key segments, themselves 60.3 -> 37.6 us over
+// no split).  Short key ranges keep the eight-wave layout, which runs a chunk
+// the same way beside decodes as alone.
+static bool few_groups_long_keys(int base, int max_keys, bool with_decodes) {
+  return with_decodes && base > 0 && base < kPfAimAlone / 4 && max_keys > kPfFewSeg;
+}
 
 void prefill_split(const ChunkList& chunks, int nq, int nkv, bool with_decodes, int* nsplit,
                    int* seg) {
-  const int G = nq / nkv;
-  int base = 0, max_keys = 0;
-  for (int i = 0; i < chunks.n; ++i) {
-    base += (chunks.c[i].len * G + kPrefillRows - 1) / kPrefillRows * nkv;
-    max_keys = max(max_keys, chunks.c[i].start_pos + chunks.c[i].len);
-  }
+  int base, max_keys;
+  chunk_extent(chunks, nq, nkv, &base, &max_keys);
   int ns = 1;
   const int aim = with_decodes ? kPfAimHybrid : kPfAimAlone;
   const int below = with_decodes ? kPfAimHybrid : kPfAimAlone / 2;
   if (base > 0 && base < below) ns = min((aim + base - 1) / base, max(1, max_keys / 256));
-  // a chunk of few row groups over a long cached prefix (a tensor-parallel
-  // share: one kv head) walks its keys in segments of at most 1024, up to the
-  // split count the workspace bound allows (Llama-2-70B-shaped T=8 share:
-  // attention 60.3 -> 37.6 us; 512-key segments were slower, their prefill
-  // workgroups crowd out the decode waves)
-  if (base > 0 && base < kPfAimAlone / 4)
-    ns = max(ns, min((max_keys + 1023) / 1024, (kPfAimAlone + base - 1) / base));
+  if (few_groups_long_keys(base, max_keys, with_decodes))
+    ns = max(ns, min((max_keys + kPfFewSeg - 1) / kPfFewSeg, (kPfAimAlone + base - 1) / base));
   ns = max(ns, 1);
   int sg = (max_keys + ns - 1) / ns;
   sg = (sg + 31) / 32 * 32;
@@ -750,8 +789,7 @@ static hipError_t run_attention(AttnArgs& A, void* pf_ws, void* dc_ws, hipStream
     A.pf_gx = (max_len * G + kPrefillRows - 1) / kPrefillRows;
     A.pf_ns = 1;
     A.pf_seg = 1 << 30;
-    // four-wave workgroups run beside many decodes only, where keys are not split
-    if (pf_ws && NW == 2 * kPfHalfWaves) {
+    if (pf_ws) {
       prefill_split(chunks, nq, nkv, dec.n > 0, &A.pf_ns, &A.pf_seg);
       if (A.pf_ns <= 1) {
         A.pf_ns = 1;
@@ -807,11 +845,13 @@ hipError_t launch_attention(const bf16* qkv, int nq, int nkv, int d, const Chunk
   // four-wave workgroup slots keeps four-wave workgroups instead: every CU
   // then holds a prefill and a decode workgroup (MFMA-bound and HBM-bound
   // waves side by side), where eight-wave prefill workgroups would take
-  // every slot and leave the decodes waiting.
-  int base = 0;
-  for (int i = 0; i < chunks.n; ++i)
-    base += (chunks.c[i].len * (nq / nkv) + kPrefillRows - 1) / kPrefillRows * nkv;
-  const bool four = dec.n > 0 && base >= kPfFourWaveFrom;
+  // every slot and leave the decodes waiting.  So does a chunk of few row
+  // groups over a long cached prefix, whose keys are then split into about
+  // one segment per CU.
+  int base, max_keys;
+  chunk_extent(chunks, nq, nkv, &base, &max_keys);
+  const bool four = (dec.n > 0 && base >= kPfFourWaveFrom) ||
+                    few_groups_long_keys(base, max_keys, dec.n > 0);
   if (d == 128)
     return four ? run_attention<128, 4>(A, pf_ws, dc_ws, s, mid)
                 : run_attention<128, 8>(A, pf_ws, dc_ws, s, mid);

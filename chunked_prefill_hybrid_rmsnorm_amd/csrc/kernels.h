@@ -56,8 +56,6 @@ hipError_t launch_gemm_residual_norm(const bf16* a, const bf16* w, bf16* h, cons
 hipError_t launch_rope_kv_append(bf16* qkv, const int32_t* pos, const int32_t* slot, int rows,
                                  int nq, int nkv, int d, float theta, const KvDev& kv,
                                  hipStream_t s);
-// Per-row RoPE table of the layer path (workspace): position, KV slot (-1:
-// none) and cos / sin of the d/2 pair angles.
 // theta^(-2 i / d) for the rotation pairs of a head (d / 2 <= kRopeMaxPairs),
 // computed on the host in fp64 and passed by value
 constexpr int kRopeMaxPairs = 64;
