@@ -25,8 +25,12 @@ K steps.
 Printed: one JSON line with tokens/s per layer (real rows / time), the
 dominant kernel's roofline figures, the time of every kernel slot of the
 layer against the roofline model T = max(T_math, T_mem), and the CPU
-oracle's rate on the host.  Kernel times come from HIP events that the
+oracle's rate on the host (median of --cpu-runs full calls, plus a one-thread
+figure on a bounded sample).  Kernel times come from HIP events that the
 library records between its kernels on the stream it launches on.
+
+``--cpu-table PATH`` only times the CPU oracle over the other measured
+configurations (no GPU use) and writes a markdown table.
 """
 from __future__ import annotations
 
@@ -62,7 +66,10 @@ def parse():
     p.add_argument("--rotate", type=int, default=4)
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-runs", type=int, default=1)
+    p.add_argument("--cpu-runs", type=int, default=3)
+    p.add_argument("--cpu-table", metavar="PATH",
+                   help="only time the CPU oracle over the sweep configurations (no GPU) and "
+                        "write the markdown table to PATH")
     p.add_argument("--no-standalone", action="store_true",
                    help="skip the stand-alone call's timing (profiling runs)")
     p.add_argument("--plain", action="store_true",
@@ -184,6 +191,76 @@ def cpu_baseline(hb, name, runs):
                                        f"cached tokens + 4 decodes (ctx U[{lo},{hi}]) of the same "
                                        f"layer and weights, M={ms}, one call {t1:.2f} s"}
     return res
+
+
+def cpu_table(runs, path):
+    """The oracle as it stands on the host cores (every BLAS thread) over the
+    configurations the GPU path is measured on: the tiny, Mistral-shaped and
+    Llama-70B-shaped batches, three points of the token-budget grid, and the
+    2048-token prompt prefilled in 1 and in 16 chunks (each chunk's call
+    reading the pages the earlier calls wrote).  Median of `runs` calls per
+    batch; one pass of each prompt."""
+    import numpy as np
+    from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
+    from oracle import layer_forward
+    from tests.oracle_inputs import oracle_args, oracle_weights, widen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    M7 = I.MISTRAL_7B
+    grid = lambda lp, bd: I.make_hybrid_batch(M7, chunk_lens=[lp] if lp else [],
+                                              chunk_starts=[0] if lp else [], n_decodes=bd,
+                                              ctx_range=(128, 4096), seed=0)
+    batches = [
+        ("tiny layer (H=256): Lp=64 (64 cached) + Bd=4", lambda: I.tiny_batch(seed=0)),
+        ("Mistral-7B-shaped: Lp=256 (768 cached) + Bd=32", lambda: I.mistral_batch(seed=0)),
+        ("Mistral-7B-shaped grid point: Lp=256 + Bd=0", lambda: grid(256, 0)),
+        ("Mistral-7B-shaped grid point: Lp=128 + Bd=128", lambda: grid(128, 128)),
+        ("Mistral-7B-shaped grid point: Lp=512 + Bd=16", lambda: grid(512, 16)),
+        ("Llama-2-70B-shaped: Lp=512 (3584 cached) + Bd=64", lambda: I.llama70_batch(seed=0)),
+    ]
+    rows = []
+    for desc, make in batches:
+        hb = make()
+        args = oracle_args(hb)
+        times = []
+        for _ in range(runs):
+            t = time.perf_counter()
+            layer_forward(*args)
+            times.append(time.perf_counter() - t)
+        t_med = sorted(times)[len(times) // 2]
+        M = hb.x.shape[0]
+        rows.append((desc, M, f"median of {runs}", t_med, M / t_med))
+        log(f"{desc}: {t_med:.3f} s/call")
+    for n in (1, 16):
+        seq = I.make_prompt_sequence(M7, 2048, n, seed=0)
+        w = oracle_weights(seq.weights)
+        kv = widen(seq.kv_pages)
+        t = time.perf_counter()
+        for k in range(n):
+            c = seq.chunk(k)
+            kv = layer_forward(seq.shape, w, widen(seq.chunk_rows(k)),
+                               [(c.length, c.start_pos, c.block_table)], [], [], kv).kv_pages
+        dt = time.perf_counter() - t
+        rows.append((f"Mistral-7B-shaped 2048-token prompt in {n} chunk(s)", 2048,
+                     f"{n} call(s), one pass", dt, 2048 / dt))
+        log(f"2048-token prompt in {n} chunk(s): {dt:.2f} s")
+    lines = ["# CPU oracle on the measured configurations", "",
+             "Command (run from the repository root):", "",
+             f"    python bench.py --cpu-table {path} --cpu-runs {runs}", "",
+             f"float64 NumPy oracle (`oracle/`), {threads} BLAS threads, host CPU "
+             f"`{_cpu_model()}` ({os.cpu_count()} logical CPUs). Seeded synthetic inputs, the "
+             "same recipes as the GPU measurements. A reported baseline, not a target.", "",
+             "| batch | rows | timing | s | tokens/s |", "|---|---:|---|---:|---:|"]
+    for desc, M, how, dt, tps in rows:
+        lines.append(f"| {desc} | {M} | {how} | {dt:.3f} | {tps:.1f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"cpu_table": path, "threads": threads,
+                      "rows": [{"batch": r[0], "rows": r[1], "seconds": round(r[3], 4),
+                                "tokens_per_s": round(r[4], 2)} for r in rows]}), flush=True)
 
 
 def measure(a, name, steps, warmup, settle_ms, graph, key):
@@ -354,6 +431,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         log("bench.py: only --gpus 1 is supported (single-GPU build)")
         sys.exit(2)
+    if a.cpu_table:
+        cpu_table(a.cpu_runs, a.cpu_table)
+        return
     import torch
     from chunked_prefill_hybrid_rmsnorm_amd import binding as B
     if not torch.cuda.is_available():
