@@ -272,7 +272,15 @@ template <int SPLITS>
 __global__ __launch_bounds__(kRopeThreads) void rope_append_wide_kernel(
     bf16* __restrict__ qkv, const float* __restrict__ part, int rows, int Mp, int nq, int nkv,
     int d, ChunkList chunks, DecDev dec, RopeFreq freq, KvDev kv) {
-  const int r = blockIdx.x;
+  // Rows go to the XCDs in contiguous runs (workgroup ids are dealt
+  // round-robin over the 8 XCDs, and the grid's x extent is a multiple of 8
+  // when it is Mp): the tokens of one KV page, whose V values share the
+  // page's dimension rows (dimension-major V), are then written through one
+  // L2, which merges them, instead of each XCD's L2 writing back its own
+  // part of every line.
+  const int nrows = gridDim.x;
+  const int per = nrows / 8, rem = nrows % 8, xcd = blockIdx.x % 8;
+  const int r = xcd * per + min(xcd, rem) + blockIdx.x / 8;
   const int tid = threadIdx.x;
   const int h0 = blockIdx.y * kRopeHeads;
   const int nh = nq + 2 * nkv;
