@@ -193,13 +193,15 @@ def cpu_baseline(hb, name, runs):
     return res
 
 
-def cpu_table(runs, path):
+def cpu_table(runs, path, keys=None, prompt_chunks=(1, 16)):
     """The oracle as it stands on the host cores (every BLAS thread) over the
     configurations the GPU path is measured on: the tiny, Mistral-shaped and
     Llama-70B-shaped batches, three points of the token-budget grid, and the
     2048-token prompt prefilled in 1 and in 16 chunks (each chunk's call
     reading the pages the earlier calls wrote).  Median of `runs` calls per
-    batch; one pass of each prompt."""
+    batch; one pass of each prompt.  `keys` picks a subset of the batches
+    (tiny, mistral, grid256, grid128d128, grid512d16, llama70) and
+    `prompt_chunks` the prompt splits."""
     import numpy as np
     from chunked_prefill_hybrid_rmsnorm_amd import inputs as I
     from oracle import layer_forward
@@ -214,15 +216,19 @@ def cpu_table(runs, path):
                                               chunk_starts=[0] if lp else [], n_decodes=bd,
                                               ctx_range=(128, 4096), seed=0)
     batches = [
-        ("tiny layer (H=256): Lp=64 (64 cached) + Bd=4", lambda: I.tiny_batch(seed=0)),
-        ("Mistral-7B-shaped: Lp=256 (768 cached) + Bd=32", lambda: I.mistral_batch(seed=0)),
-        ("Mistral-7B-shaped grid point: Lp=256 + Bd=0", lambda: grid(256, 0)),
-        ("Mistral-7B-shaped grid point: Lp=128 + Bd=128", lambda: grid(128, 128)),
-        ("Mistral-7B-shaped grid point: Lp=512 + Bd=16", lambda: grid(512, 16)),
-        ("Llama-2-70B-shaped: Lp=512 (3584 cached) + Bd=64", lambda: I.llama70_batch(seed=0)),
+        ("tiny", "tiny layer (H=256): Lp=64 (64 cached) + Bd=4", lambda: I.tiny_batch(seed=0)),
+        ("mistral", "Mistral-7B-shaped: Lp=256 (768 cached) + Bd=32",
+         lambda: I.mistral_batch(seed=0)),
+        ("grid256", "Mistral-7B-shaped grid point: Lp=256 + Bd=0", lambda: grid(256, 0)),
+        ("grid128d128", "Mistral-7B-shaped grid point: Lp=128 + Bd=128", lambda: grid(128, 128)),
+        ("grid512d16", "Mistral-7B-shaped grid point: Lp=512 + Bd=16", lambda: grid(512, 16)),
+        ("llama70", "Llama-2-70B-shaped: Lp=512 (3584 cached) + Bd=64",
+         lambda: I.llama70_batch(seed=0)),
     ]
     rows = []
-    for desc, make in batches:
+    for key, desc, make in batches:
+        if keys is not None and key not in keys:
+            continue
         hb = make()
         args = oracle_args(hb)
         times = []
@@ -234,7 +240,7 @@ def cpu_table(runs, path):
         M = hb.x.shape[0]
         rows.append((desc, M, f"median of {runs}", t_med, M / t_med))
         log(f"{desc}: {t_med:.3f} s/call")
-    for n in (1, 16):
+    for n in prompt_chunks:
         seq = I.make_prompt_sequence(M7, 2048, n, seed=0)
         w = oracle_weights(seq.weights)
         kv = widen(seq.kv_pages)
