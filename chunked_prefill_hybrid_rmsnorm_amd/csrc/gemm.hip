@@ -184,7 +184,8 @@ struct Choice {
 
 // Split K (powers of two, at most 8, at least 8 k-steps per split) while the
 // workgroup count stays within one per CU.  The reduce kernels are
-// instantiated for 2, 4 and 8 splits.
+// instantiated for 2, 4 and 8 splits, and the plain reduce and the RoPE step
+// (which sums the QKV partials) also for 3, 5, 6 and 7 (small-batch QKV).
 static int splits_for(int tiles, int ksteps) {
   int sp = 1;
   while (tiles * sp * 2 <= 256 && ksteps / (sp * 2) >= 8 && sp < 8) sp *= 2;
@@ -269,6 +270,16 @@ static Choice choose(GemmEpilogue epi, int mp, int n, int k) {
   }
   const int t128 = mt * ((n + 127) / 128);
   c.splits = splits_for(t128, ksteps);
+  if (!c.big && epi == EPI_STORE) {
+    // plain GEMMs of small batches (the QKV projection of decode-heavy
+    // batches, whose partials the RoPE step sums): the most splits, up to 8
+    // and not only powers of two, that keep one round of 256 workgroups and
+    // >= 8 k-steps per split (48 column tiles: 5 splits, 240 workgroups
+    // instead of 4 splits and 192)
+    for (int s = c.splits + 1; s <= 8; ++s)
+      if (t128 * s <= 256 && ksteps / s >= 8) c.splits = s;
+    return c;
+  }
   // residual GEMMs with short k loops (the O projection): 64-column tiles
   // need half the K splits, so half the fp32 partials to write and reduce,
   // which outweighs re-reading A for twice as many column tiles (and where
@@ -410,7 +421,11 @@ hipError_t launch_gemm(GemmEpilogue epi, const bf16* a, const bf16* w, const bf1
     else HL_REDUCE(EPI_RESIDUAL, 8);
   } else {
     if (ch.splits == 2) HL_REDUCE(EPI_STORE, 2);
+    else if (ch.splits == 3) HL_REDUCE(EPI_STORE, 3);
     else if (ch.splits == 4) HL_REDUCE(EPI_STORE, 4);
+    else if (ch.splits == 5) HL_REDUCE(EPI_STORE, 5);
+    else if (ch.splits == 6) HL_REDUCE(EPI_STORE, 6);
+    else if (ch.splits == 7) HL_REDUCE(EPI_STORE, 7);
     else HL_REDUCE(EPI_STORE, 8);
   }
 #undef HL_REDUCE

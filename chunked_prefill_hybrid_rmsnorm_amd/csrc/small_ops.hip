@@ -373,7 +373,11 @@ hipError_t launch_rope_append_wide(bf16* qkv, const float* part, int splits, int
                      Mp, nq, nkv, d, chunks, dec, freq, kv)
   if (!part) HL_ROPE(0);
   else if (splits == 2) HL_ROPE(2);
+  else if (splits == 3) HL_ROPE(3);
   else if (splits == 4) HL_ROPE(4);
+  else if (splits == 5) HL_ROPE(5);
+  else if (splits == 6) HL_ROPE(6);
+  else if (splits == 7) HL_ROPE(7);
   else if (splits == 8) HL_ROPE(8);
   else return hipErrorInvalidValue;
 #undef HL_ROPE

@@ -167,6 +167,18 @@ def test_gemm_entries_reject_before_launch(lib):
     assert s(None, fake, fake, fake, 16, 64, 64, None) == -1
 
 
+@pytest.mark.parametrize("mp,n,k,splits", [(64, 6144, 4096, 5), (64, 10240, 8192, 3),
+                                             (32, 4608, 4096, 7), (128, 4096, 4096, 8),
+                                             (288, 6144, 4096, 4)])
+def test_gemm_split_counts(lib, mp, n, k, splits):
+    """The GEMM workspace is the fp32 partials of the chosen split count:
+    small batches take the most splits (up to 8, any count) that keep one
+    round of 256 workgroups and >= 8 k-steps each for the plain epilogue
+    (48, 80 and 36 column tiles of 128: 5, 3 and 7 splits; 32 tiles: 8);
+    288-row tiles keep powers of two."""
+    assert B.hl_gemm_workspace_bytes(mp, n, k) == splits * mp * n * 4
+
+
 def test_kv_layout_roundtrip():
     import numpy as np
     rng = np.random.default_rng(0)

@@ -95,7 +95,13 @@ def test_rmsnorm_step():
                                             # 128 columns on 256-row tiles, 4 K splits
                                             (500, 512, 4096, 4096, True),
                                             # 224 columns (plain only)
-                                            (570, 576, 13440, 2048, True)])
+                                            (570, 576, 13440, 2048, True),
+                                            # small batches, split counts that are not
+                                            # powers of two for the plain epilogue: 5
+                                            # (48 column tiles), 3 (80) and 7 (36)
+                                            (60, 64, 6144, 4096, True),
+                                            (50, 64, 10240, 8192, True),
+                                            (30, 32, 4608, 4096, True)])
 def test_gemm_step(m, mp, n, k, split):
     """Without a workspace K is not split (one launch, the long-k tile with two
     k-groups for the 288-row shapes); with one the partials are reduced."""
