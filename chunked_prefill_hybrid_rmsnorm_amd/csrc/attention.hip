@@ -38,7 +38,7 @@ constexpr int kPfRowsPerWave = 32;                         // two 16-row MFMA bl
 constexpr int kPrefillRows = kPfRowsPerWave * kPfHalfWaves;  // rows per prefill workgroup
 constexpr int kPfStages = 3;                             // LDS ring depth of prefill K/V
 constexpr bool kPfPipelined = true;  // prefill waves score the next step during this step's softmax
-constexpr int kDecMinSliceSteps = 6;   // fewest 32-key steps in a decode slice
+constexpr int kDecMinSliceSteps = 4;   // fewest 32-key steps in a decode slice
 constexpr int kDecMaxWaves = 4096;     // decode waves of one launch, all kv heads
 
 struct AttnArgs {

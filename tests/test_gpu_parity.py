@@ -197,9 +197,9 @@ def test_layer_edge_cases(name):
 @pytest.mark.parametrize("shape", [TINY, D128], ids=["d64", "d128"])
 def test_merge_of_many_parts(shape, prefix, ctx):
     """A 16-row chunk after a long cached prefix beside one long decode.  With
-    6000 cached tokens (21 or 23 key segments) and a 4000-token decode (21
+    6000 cached tokens (21 or 23 key segments) and a 4000-token decode (31
     slices) the rows have 17 to 32 parts, which the merge loads in one round
-    with one lane per part; with 20000 (40 or 64 segments) and 8000 (41
+    with one lane per part; with 20000 (40 or 64 segments) and 8000 (62
     slices) they have more than 32 and take its two-pass path."""
     _flush(f"merge of many parts, head dim {shape.head_dim}, prefix {prefix}, decode ctx {ctx}")
     hb = make_hybrid_batch(shape, chunk_lens=[16], chunk_starts=[prefix], ctx_lens=[ctx, 9],
