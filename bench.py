@@ -26,7 +26,9 @@ Printed: one JSON line with tokens/s per layer (real rows / time), the
 dominant kernel's roofline figures, the time of every kernel slot of the
 layer against the roofline model T = max(T_math, T_mem), and the CPU
 oracle's rate on the host (median of --cpu-runs full calls, plus a one-thread
-figure on a bounded sample).  Kernel times come from HIP events that the
+figure on a bounded sample), and the HBM read rate a plain streaming read
+attains on this GPU (`hbm_read_attained`; an HBM-bound dominant kernel also
+gets its fraction of that rate).  Kernel times come from HIP events that the
 library records between its kernels on the stream it launches on.
 
 ``--cpu-table PATH`` only times the CPU oracle over the other measured
@@ -269,6 +271,34 @@ def cpu_table(runs, path, keys=None, prompt_chunks=(1, 16)):
                                 "tokens_per_s": round(r[4], 2)} for r in rows]}), flush=True)
 
 
+def hbm_read_attained(gib=1, copies=4, calls=16):
+    """HBM read rate of the library's plain streaming read (hl_read_stream)
+    over `copies` buffers of `gib` GiB read in turn, together far past the
+    256 MB MALL: the bandwidth this GPU attains, beside the 8 TB/s of the data
+    sheet that `roofline.peak` uses."""
+    import torch
+    from chunked_prefill_hybrid_rmsnorm_amd import binding as B
+    n = gib << 30
+    bufs = [torch.full((n // 4,), 0x01020304, dtype=torch.int32, device="cuda")
+            for _ in range(copies)]
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        B.hl_read_stream(b, n, sink)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(calls):
+        B.hl_read_stream(bufs[i % copies], n, sink)
+    t1.record()
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) * 1e-3
+    del bufs
+    torch.cuda.empty_cache()
+    return {"value": round(n * calls / sec / 1e12, 3), "unit": "TB/s", "bytes_per_call": n,
+            "calls": calls, "buffers": copies,
+            "kernel": "hl_read_stream: 16-byte non-temporal loads, 8192 workgroups x 256 lanes"}
+
+
 def measure(a, name, steps, warmup, settle_ms, graph, key):
     """Layer time, graph replay, per-call spread, per-slot times and the
     dominant slot's roofline for one workload."""
@@ -488,6 +518,13 @@ def main():
         "standalone_call": r["standalone_call"],
         "extra": extra,
     }
+    log("timing the streaming read ...")
+    att = hbm_read_attained()
+    result["hbm_read_attained"] = att
+    if r["roofline"] and r["roofline"].get("bound") == "hbm":
+        # the dominant kernel's rate against the attained read rate as well
+        result["roofline"]["frac_of_attained"] = round(
+            r["roofline"]["achieved"] / (att["value"] * 1e3), 4)
     if not a.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(hb, a.workload, a.cpu_runs)

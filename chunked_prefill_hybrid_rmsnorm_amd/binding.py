@@ -108,6 +108,7 @@ _SIGS = {
                                  _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
     "hl_argmax_rows": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_void_p]),
+    "hl_read_stream": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_void_p]),
     "hl_rope_kv_append": (_c.c_int, [_P(hl_config), _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                      _c.c_int32, _P(hl_kv), _c.c_void_p]),
     "hl_prefill_attention": (_c.c_int, [_P(hl_config), _c.c_void_p, _P(hl_chunk), _c.c_int32,
@@ -343,6 +344,10 @@ def hl_argmax_rows(logits, rows, vocab, sample_req, sample_pos, last_tok, out_to
     _check(load().hl_argmax_rows(_ptr(logits), rows, vocab, _ptr(sample_req), _ptr(sample_pos),
                                  _ptr(last_tok), last_tok.numel(), _ptr(out_tokens),
                                  out_tokens.numel(), _stream(stream)), "hl_argmax_rows")
+
+
+def hl_read_stream(buf, nbytes, sink, stream=None):
+    _check(load().hl_read_stream(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "hl_read_stream")
 
 
 def hl_rope_kv_append(cfg, qkv, positions, slots, rows, kv: hl_kv, stream=None):

@@ -324,6 +324,21 @@ int hl_argmax_rows(const hl_bf16* logits, int32_t rows, int32_t vocab, const int
                    const int32_t* sample_pos, int32_t* last_tok, int32_t n_last,
                    int32_t* out_tokens, int32_t n_out, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid.
+ */
+
+/* Reads the `bytes` bytes at buf once, with the plainest streaming pattern
+ * (16-byte non-temporal vector loads, 8192 workgroups of 256 lanes, eight
+ * loads in flight per lane).  Workgroup b stores the XOR of the 32-bit words
+ * it read to sink[b], so the XOR of sink[0..8192) is that of the whole
+ * buffer.  Timed over buffers larger than the 256 MB MALL it gives the HBM
+ * read rate this GPU attains, the bandwidth term of the roofline
+ * (Sarathi-Serve digest, section 4) as measured rather than as specified.
+ * buf device, 16-byte aligned; bytes a positive multiple of 256 MiB
+ * (HL_ERR_SHAPE otherwise); sink device uint32 [8192]. */
+int hl_read_stream(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

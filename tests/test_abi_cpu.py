@@ -179,6 +179,18 @@ def test_gemm_split_counts(lib, mp, n, k, splits):
     assert B.hl_gemm_workspace_bytes(mp, n, k) == splits * mp * n * 4
 
 
+def test_read_stream_rejects_before_launch(lib):
+    """The streaming-read measurement entry checks its arguments before any
+    launch (fake device pointers, no GPU needed)."""
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.hl_read_stream
+    assert f(None, 256 << 20, fake, None) == -1
+    assert f(fake, 256 << 20, None, None) == -1
+    assert f(fake, 0, fake, None) == -2
+    assert f(fake, (256 << 20) + 16, fake, None) == -2   # not a multiple of 256 MiB
+    assert f(ctypes.c_void_p(0x1008), 256 << 20, fake, None) == -2   # not 16-byte aligned
+
+
 def test_kv_layout_roundtrip():
     import numpy as np
     rng = np.random.default_rng(0)

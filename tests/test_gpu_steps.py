@@ -1,6 +1,7 @@
 """Per-step GPU parity of the stand-alone entry points that the layer call
 does not route through: hl_rope_kv_append and hl_decode_attention, each
-through the C ABI against the oracle's pieces on seeded inputs.
+through the C ABI against the oracle's pieces on seeded inputs; and the
+streaming-read measurement aid against a host XOR.
 
 Floating point within 2e-2 * max|ref| per tensor; copied bf16 values (V) and
 every KV slot or output row the step must not touch bit-exact."""
@@ -166,3 +167,23 @@ def test_decode_attention_step(name, ctx):
             for h in range(nq):
                 np.testing.assert_allclose(got[j, h * d:(h + 1) * d], kv64[page, 1, h // G, 0],
                                            rtol=2 ** -8, atol=0)
+
+
+# ---------------------------------------------------------------- streaming read (measurement aid)
+def test_read_stream_reads_every_word_once():
+    """hl_read_stream leaves one XOR per workgroup: over 512 MiB of seeded
+    random words the XOR of the 8192 results equals the XOR of the buffer
+    computed on the host, and every word of the result array is written."""
+    import torch
+    print("streaming read over 512 MiB", flush=True)
+    n = (512 << 20) // 4
+    g = torch.Generator(device="cpu").manual_seed(7)
+    host = torch.randint(-(1 << 31), (1 << 31) - 1, (n,), dtype=torch.int32, generator=g)
+    buf = host.to("cuda")
+    sink = torch.full((8192 + 1,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    B.hl_read_stream(buf, n * 4, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    want = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
+    assert int(np.bitwise_xor.reduce(got[:8192])) == want
+    assert got[8192] == 0x5A5A5A5A, "wrote past the 8192 results"
