@@ -36,9 +36,15 @@ namespace hl {
 constexpr int kPfHalfWaves = 4;  // waves of one prefill group
 constexpr int kPfRowsPerWave = 32;                         // two 16-row MFMA blocks
 constexpr int kPrefillRows = kPfRowsPerWave * kPfHalfWaves;  // rows per prefill workgroup
-constexpr int kPfStages = 3;                             // LDS ring depth of prefill K/V
+// LDS ring of prefill K/V: kPfStages slots, copies issued kPfAhead steps
+// ahead of the step being opened.  A copy then lands in the slot of step t - 2,
+// whose fragments every wave has used (not only read) before the barrier
+// that opens step t, so the barrier needs no wait for outstanding LDS reads.
+constexpr int kPfStages = 4;
+constexpr int kPfAhead = 2;
 constexpr bool kPfPipelined = true;  // prefill waves score the next step during this step's softmax
 constexpr int kDecMinSliceSteps = 4;   // fewest 32-key steps in a decode slice
+constexpr int kDecSlotsPerWave = 4;    // wave slots of the free workgroups per decode wave
 constexpr int kDecMaxWaves = 4096;     // decode waves of one launch, all kv heads
 
 struct AttnArgs {
@@ -59,7 +65,7 @@ struct AttnArgs {
   int dc_row0;   // first decode row
   int dc_slices;  // slices per kv head the grid provides (upper bound of P)
   int dc_pn;      // partial slots per q head = dc_slices + n
-  int dc_wgs;     // decode workgroups = ceil(dc_slices * nkv / waves per workgroup)
+  int dc_wgs;     // decode workgroups = min(free workgroups, dc_slices * nkv)
   float* dc_o;
   float* dc_ml;
   int merge_row0;  // first row the merge grid covers (chunk rows only when keys were split)
@@ -243,8 +249,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
   init_acc<D>(a[0]);
   init_acc<D>(a[1]);
   const float scale = kAttnLog2e * rsqrtf((float)D);
-  static_assert(kPfStages >= 3 && kPfStages <= 4, "the waits below allow 0 .. 2 steps in flight");
-  for (int s = 0; s + 1 < kPfStages; ++s)
+  static_assert(kPfAhead >= 1 && kPfAhead <= 3 && kPfStages >= kPfAhead + 1,
+                "the waits below allow 0 .. 2 later steps in flight");
+  for (int s = 0; s < kPfAhead; ++s)
     if (s < my_n) issue(s);
   if constexpr (kPfPipelined) {
     // Each wave runs one step ahead of its softmax: while step i's softmax
@@ -253,22 +260,24 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
     // busy together instead of in turn.  Stage t is waited for, and its
     // copies made visible by the barrier, before any of its fragments are
     // read; the copies issued after that barrier refill the slot of stage
-    // t-1, whose reads (the previous iteration's) this wave has seen land.
+    // t - 2, whose V fragments every wave consumed in the previous iteration
+    // (with a ring one slot shorter it would be stage t - 1, whose V reads
+    // may still be in flight, and the barrier would first wait for them).
     // Every wave passes my_n barriers, then one per step the other group has
     // beyond them.
     auto open_stage = [&](int t) {
-      const int after = min(kPfStages - 2, my_n - 1 - t);  // later stages that may be in flight
+      const int after = min(kPfAhead - 1, my_n - 1 - t);  // later stages that may be in flight
       if (after >= 2)
         wait_vmcnt<2 * PfStage<D>::PER_WAVE>();
       else if (after == 1)
         wait_vmcnt<PfStage<D>::PER_WAVE>();
       else
         wait_vmcnt<0>();
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      if constexpr (kPfStages < kPfAhead + 2) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (t + kPfStages - 1 < my_n) issue(t + kPfStages - 1);
+      if (t + kPfAhead < my_n) issue(t + kPfAhead);
     };
     KvFrag<D> fk, fv;  // K of the step being scored; V of the step being summed
     f32x4 sc[2][2];    // scores of the step whose softmax is next
@@ -322,9 +331,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
     // off the loop: one copy of the step code in the loop keeps the register
     // budget) may have V to mask.
     auto step = [&](int i, auto last) {
-      // this step's copies have landed; those of up to kPfStages - 2 later
+      // this step's copies have landed; those of up to kPfAhead - 1 later
       // steps may still be in flight
-      const int ahead = min(kPfStages - 2, my_n - 1 - i);
+      const int ahead = min(kPfAhead - 1, my_n - 1 - i);
       if (ahead >= 2)
         wait_vmcnt<2 * PfStage<D>::PER_WAVE>();
       else if (ahead == 1)
@@ -334,9 +343,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& A, int b, int wave
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      // into the slot of step i - 1, which every wave finished reading before
-      // this barrier
-      if (i + kPfStages - 1 < my_n) issue(i + kPfStages - 1);
+      // into the slot of step i + kPfAhead - kPfStages, which every wave
+      // finished reading before this barrier
+      if (i + kPfAhead < my_n) issue(i + kPfAhead);
       if (!busy) return;
       KvFrag<D> f;
       prefill_frags<D>(f, ring + (i % kPfStages) * PfStage<D>::BYTES, l16, q);
@@ -801,13 +810,18 @@ static hipError_t run_attention(AttnArgs& A, void* pf_ws, void* dc_ws, hipStream
     A.pf_ml = A.pf_ns > 1 ? A.pf_o + (size_t)A.pf_ns * chunks.n_rows * nq * D : nullptr;
   }
   if (dec.n > 0) {
-    // decode waves fill the workgroup slots the prefill part leaves free, so
-    // that both kinds run side by side (at least a quarter of the slots)
+    // decode workgroups take the slots the prefill part leaves free (at least
+    // a quarter of them), so that both kinds run side by side, with one busy
+    // decode wave per kDecSlotsPerWave wave slots: fewer, longer slices than
+    // one per slot keep HBM as busy with fewer loads queued in each CU's
+    // memory path (where the prefill copies wait behind them) and fewer
+    // partials to merge.  The busy waves spread evenly over the workgroups.
     const int slots = attention_slots<D, NW>();
     const int free_wgs = max(slots - A.pf_wgs, slots / 4);
-    A.dc_slices = max(1, min(free_wgs * NW / nkv, decode_slice_cap(dec.n, nkv, dec.max_ctx)));
+    A.dc_slices = max(1, min(free_wgs * NW / (kDecSlotsPerWave * nkv),
+                             decode_slice_cap(dec.n, nkv, dec.max_ctx)));
     A.dc_pn = A.dc_slices + dec.n;
-    A.dc_wgs = (A.dc_slices * nkv + NW - 1) / NW;
+    A.dc_wgs = min(free_wgs, A.dc_slices * nkv);
     A.dc_o = reinterpret_cast<float*>(dc_ws);
     A.dc_ml = A.dc_o + (size_t)nq * A.dc_pn * D;
   }
