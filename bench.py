@@ -366,6 +366,20 @@ def measure(a, name, steps, warmup, settle_ms, graph, key):
         g_res = {"ms_per_step": round(gms, 5), "value": round(M / (gms / 1e3), 1),
                  "calls_per_graph": len(copies)}
         log(f"layer (graph replay, {len(copies)} calls per graph) {gms * 1e3:.1f} us/step")
+        # eager calls and replays in alternating blocks, so that a clock that
+        # drifts over the run weighs on both alike; medians over the rounds
+        blk = max(1, steps // 4 // len(copies)) * len(copies)
+        e_t, g_t = [], []
+        for _ in range(4):
+            e_t.append(time_loop(layer, blk, 0))
+            g_t.append(time_loop(lambda i: g.replay(), blk // len(copies), 0) / len(copies))
+        med = lambda v: (sorted(v)[1] + sorted(v)[2]) / 2  # noqa: E731  (four rounds)
+        e_med, g_med = med(e_t), med(g_t)
+        g_res["interleaved"] = {"eager_ms_per_step": round(e_med, 5),
+                                "replay_ms_per_step": round(g_med, 5), "rounds": 4,
+                                "calls_per_block": blk}
+        log(f"interleaved blocks of {blk} calls: eager {e_med * 1e3:.1f} us/step, "
+            f"graph replay {g_med * 1e3:.1f} us/step")
 
     # spread of single calls: one event between consecutive calls
     bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
