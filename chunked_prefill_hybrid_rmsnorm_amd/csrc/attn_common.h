@@ -27,11 +27,22 @@ constexpr float kAttnLog2e = 1.4426950408889634f;
 __device__ __forceinline__ int step_key(int hp, int r) { return 8 * (r >> 2) + 4 * hp + (r & 3); }
 
 // max / sum over the four lanes l16, l16 + 16, l16 + 32, l16 + 48 (one row)
+//
+// The max of two swapped halves is one v_max_f32 written out: through
+// fmaxf the compiler cannot tell that bits coming back from a permlane are a
+// canonical float and first passes each operand through another max with
+// itself (two extra vector instructions per swap, four per row block and
+// step).  A plain VALU instruction with register operands; no memory access.
+__device__ __forceinline__ float max_bits(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float quad_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max_bits(a[0], a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_bits(b[0], b[1]);
 }
 __device__ __forceinline__ float quad_sum(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
