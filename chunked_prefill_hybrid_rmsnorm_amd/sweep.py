@@ -16,7 +16,12 @@ curve for the library on the GPU it runs on:
 4. a scan of Lp = 16 ... 1024 in steps of 16 (Bd = 0).  The time climbs in
    steps, where the GEMMs need one more row tile; the last Lp before each
    step (a plateau end) is where a token budget gets the most rows for the
-   time, so those are the candidates for the budget.
+   time, so those are the candidates for the budget;
+5. the Bd decodes alone (Lp = 0), so that the grid's piggybacked decodes can
+   be set against a separate decode call: what adding Bd decodes to a chunk
+   costs (hybrid minus chunk alone) against what they cost on their own.
+   The pages' case for piggybacking is that the first is much smaller,
+   because the decode rows ride on the chunk's weight stream.
 
 Inputs are seeded and synthetic (weights N(0, 0.02), activations and cached
 K/V N(0, 1)); one page pool holds every request, so each point only changes
@@ -203,12 +208,16 @@ def run(args) -> dict:
     kvB = pool.shape.kv_bytes_per_token
     log("warming up ...")
     point(pool, 256, 32, 16, args.warm_calls, 0)
-    res: dict = {"grid": {}, "pad_step": {}, "n_chunks": {}, "scan": {}}
+    res: dict = {"grid": {}, "pad_step": {}, "n_chunks": {}, "scan": {}, "decode_only": {}}
     for lp in LPS:
         for bd in BDS:
             ms = point(pool, lp, bd, 16, args.steps, args.warmup)
             res["grid"][f"{lp},{bd}"] = ms
             log(f"  Lp={lp:4d} Bd={bd:4d}: {ms * 1e3:7.1f} us")
+    for bd in BDS[1:]:
+        ms = point(pool, 0, bd, 16, args.steps, args.warmup)
+        res["decode_only"][str(bd)] = ms
+        log(f"  Lp=   0 Bd={bd:4d}: {ms * 1e3:7.1f} us")
     for lp in (256, 257):
         for pad in PADS:
             ms = point(pool, lp, 0, pad, args.steps, args.warmup)
@@ -255,6 +264,21 @@ def write_md(path: str, res: dict, command: str) -> None:
     for lp in LPS:
         L.append(f"| {lp} | " + " | ".join(
             f"{(lp + bd) / (res['grid'][f'{lp},{bd}'] * 1e-3) / 1e6:.2f} M" for bd in BDS) + " |")
+    if res.get("decode_only"):
+        L += ["", "## Piggybacked decodes against a separate decode call", "",
+              "Cost of adding the Bd decodes to the chunk (hybrid call minus the chunk alone), "
+              "against the Bd decodes in a call of their own (Lp = 0), us:", "",
+              "| Lp \\ Bd | " + " | ".join(str(b) for b in BDS[1:]) + " |",
+              "|---|" + "---:|" * len(BDS[1:]),
+              "| alone (Lp = 0) | " + " | ".join(us(res["decode_only"][str(bd)])
+                                                for bd in BDS[1:]) + " |"]
+        for lp in LPS:
+            base = res["grid"][f"{lp},0"]
+            L.append(f"| {lp} | " + " | ".join(
+                f"+{us(res['grid'][f'{lp},{bd}'] - base)} "
+                f"({(res['grid'][f'{lp},{bd}'] - base) / res['decode_only'][str(bd)]:.2f})"
+                for bd in BDS[1:]) + " |")
+        L += ["", "In parentheses: the added cost as a fraction of the separate decode call."]
     L += ["", "## Tile step: 256 vs 257 rows (Bd = 0)", "",
           "| pad | Lp=256 us | Lp=257 us | step |", "|---:|---:|---:|---:|"]
     for pad in PADS:
