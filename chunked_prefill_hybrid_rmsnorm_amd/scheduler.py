@@ -131,3 +131,30 @@ class StallFreeScheduler:
         for r in b.decodes:
             R[r].generated += 1
         self.running = [r for r in self.running if not R[r].done]
+
+
+def max_batch(mem_gpu: int, mem_static: int, max_seq_len: int, kv_bytes_per_token: int,
+              reserve: float = 0.0) -> int:
+    """Most requests whose KV cache fits on the GPU at once.
+
+    intelliparadigm.com article, section 4.1 (batch capacity): the batch size
+    is the memory left after the model's parameters, divided by what one
+    request's cache takes at the longest sequence,
+    ``B = floor((MG - MS) / (L * mkv))`` with MG the GPU memory available, MS
+    the parameters, L the longest sequence and mkv the KV bytes of one token
+    (every layer).  The article keeps a share of the memory free against
+    fragmentation (a fifth in its deployments); ``reserve`` is that share,
+    taken off MG first.  Integer arithmetic, so the floor is exact.
+    """
+    if not 0.0 <= reserve < 1.0:
+        raise ValueError("reserve must be in [0, 1)")
+    if min(mem_gpu, mem_static, max_seq_len, kv_bytes_per_token) < 0 or \
+            max_seq_len == 0 or kv_bytes_per_token == 0:
+        raise ValueError("sizes must be non-negative and L, mkv positive")
+    usable = mem_gpu - int(round(mem_gpu * reserve)) - mem_static
+    return max(0, usable // (max_seq_len * kv_bytes_per_token))
+
+
+def kv_bytes_per_token_model(shape, n_layers: int) -> int:
+    """mkv of a model: one token's K and V for every kv head of every layer."""
+    return shape.kv_bytes_per_token * n_layers

@@ -113,3 +113,32 @@ def test_chunk_count_capped_at_the_layer_limit():
     s2 = StallFreeScheduler(prompts, 2, 512, max_chunks=5)
     b = s2.next_batch()
     assert len(b.chunks) == 5 and b.n_rows == 15
+
+
+def test_max_batch_capacity_formula():
+    """B = floor((MG - MS) / (L * mkv)) (intelliparadigm.com article, section
+    4.1), pinned on hand-computed values."""
+    from chunked_prefill_hybrid_rmsnorm_amd.scheduler import kv_bytes_per_token_model, max_batch
+    from chunked_prefill_hybrid_rmsnorm_amd.inputs import MISTRAL_7B
+    # one token of a 32-layer Mistral-7B-shaped model: 2 (K, V) x 8 kv heads x 128 x 2 B x 32
+    mkv = kv_bytes_per_token_model(MISTRAL_7B, 32)
+    assert mkv == 131072
+    # 288 GB card, 14.5 GB of bf16 parameters, 4096-token sequences:
+    # (288e9 - 14.5e9) / (4096 * 131072) = 509.4... -> 509
+    assert max_batch(288 * 10**9, 145 * 10**8, 4096, mkv) == 509
+    # exact multiples land on the boundary, one byte less drops one request
+    assert max_batch(10 * 4096 * mkv, 0, 4096, mkv) == 10
+    assert max_batch(10 * 4096 * mkv - 1, 0, 4096, mkv) == 9
+    # a fifth kept free: (0.8 * 288e9 - 14.5e9) / 536870912 = 402.1... -> 402
+    assert max_batch(288 * 10**9, 145 * 10**8, 4096, mkv, reserve=0.2) == 402
+    # parameters filling the card leave no room (never negative)
+    assert max_batch(10**9, 2 * 10**9, 4096, mkv) == 0
+
+
+def test_max_batch_rejects_bad_sizes():
+    import pytest
+    from chunked_prefill_hybrid_rmsnorm_amd.scheduler import max_batch
+    with pytest.raises(ValueError):
+        max_batch(100, 0, 0, 8)
+    with pytest.raises(ValueError):
+        max_batch(100, 0, 8, 8, reserve=1.0)
