@@ -29,7 +29,10 @@ oracle's rate on the host (median of --cpu-runs full calls, plus a one-thread
 figure on a bounded sample), and the HBM read rate a plain streaming read
 attains on this GPU (`hbm_read_attained`; an HBM-bound dominant kernel also
 gets its fraction of that rate).  Kernel times come from HIP events that the
-library records between its kernels on the stream it launches on.
+library records between its kernels on the stream it launches on.  `parts`
+times the batch's chunk and its decodes as separate calls beside the hybrid
+call (alternating rounds): the saving of one hybrid call over the two, and
+what the piggybacked decodes add as a fraction of their own call.
 
 ``--cpu-table PATH`` only times the CPU oracle over the other measured
 configurations (no GPU use) and writes a markdown table.
@@ -74,6 +77,8 @@ def parse():
                         "write the markdown table to PATH")
     p.add_argument("--no-standalone", action="store_true",
                    help="skip the stand-alone call's timing (profiling runs)")
+    p.add_argument("--no-parts", action="store_true",
+                   help="skip timing the batch's chunk and its decodes as separate calls")
     p.add_argument("--plain", action="store_true",
                    help="time the stand-alone layer call instead of the call inside a stack")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -468,11 +473,68 @@ def measure(a, name, steps, warmup, settle_ms, graph, key):
         pms = time_loop(plain, max(steps // 2, 1), max(warmup // 2, 1))
         other = {"ms_per_step": round(pms, 5), "value": round(M / (pms / 1e3), 1)}
         log(f"stand-alone call (own first RMSNorm) {pms * 1e3:.1f} us/step")
+    parts = None
+    if not a.plain and not a.no_parts and hb.chunks and db.dec.n > 0:
+        parts = time_parts(db, hb, copies, steps, a.pad)
+        log(f"parts: hybrid {parts['hybrid_ms'] * 1e3:.1f} us, chunk alone "
+            f"{parts['chunk_alone_ms'] * 1e3:.1f} us, decodes alone "
+            f"{parts['decodes_alone_ms'] * 1e3:.1f} us")
     return hb, desc, {
         "ms": ms, "tok_s": tok_s, "M": M, "Mp": db.Mp, "roofline": roof, "stages": table,
         "layer_roofline": {"t_roof_us": round(t_roof * 1e6, 2), "t_us": round(ms * 1e3, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
-        "graph_replay": g_res, "per_call": spread, "standalone_call": other}
+        "graph_replay": g_res, "per_call": spread, "standalone_call": other, "parts": parts}
+
+
+def time_parts(db, hb, copies, steps, pad):
+    """The hybrid call against its parts: the chunk rows alone and the decode
+    rows alone, each as a call inside a layer stack on the same weights,
+    pages and contexts, timed in three alternating rounds (medians), so that
+    clock drift weighs on all three alike.  The pages' claim is that the
+    decodes cost far less piggybacked on the chunk than in a call of their own
+    (Sarathi-Serve digest, section 2; intelliparadigm.com article, section 3.1)."""
+    import torch
+    from chunked_prefill_hybrid_rmsnorm_amd import binding as B
+    H = hb.shape.hidden
+    Lp = sum(c.length for c in hb.chunks)
+    M = db.M
+    none = B.hl_decodes(0, None, None, 0, 0)
+
+    def setup(x_rows):
+        m = x_rows.shape[0]
+        mp = -(-m // pad) * pad
+        xn = torch.empty((mp, H), dtype=torch.bfloat16, device="cuda")
+        B.hl_rmsnorm(x_rows, db.wt["g_attn"], xn, m, mp, H, hb.shape.rms_eps)
+        return xn, torch.empty_like(xn), torch.empty_like(x_rows)
+
+    full = (db.x, db.chunks, db.dec) + setup(db.x)
+    chunk = (db.x[:Lp], db.chunks, none) + setup(db.x[:Lp])
+    decs = (db.x[Lp:M], [], db.dec) + setup(db.x[Lp:M])
+
+    def caller(spec):
+        x, chunks, dec, xn_in, xn_next, out = spec
+
+        def call(i):
+            (wt, ws), kv = copies[i % len(copies)]
+            B.hl_layer_forward_chain(db.cfg, ws, x, chunks, dec, kv, out, db.ws, db.ws_bytes,
+                                     pad, xn_in=xn_in, g_next=wt["g_attn"], xn_next=xn_next)
+        return call
+
+    calls = [caller(full), caller(chunk), caller(decs)]
+    blk = max(len(copies), steps // 4 // len(copies) * len(copies))
+    for c in calls:  # warm each call (one round of the rotation copies)
+        for i in range(len(copies)):
+            c(i)
+    t = [[], [], []]
+    for _ in range(3):
+        for k, c in enumerate(calls):
+            t[k].append(time_loop(c, blk, 0))
+    med = [sorted(v)[1] for v in t]
+    return {"hybrid_ms": round(med[0], 5), "chunk_alone_ms": round(med[1], 5),
+            "decodes_alone_ms": round(med[2], 5),
+            "saving": round(1 - med[0] / (med[1] + med[2]), 4),
+            "decodes_added_frac": round((med[0] - med[1]) / med[2], 4),
+            "rounds": 3, "calls_per_block": blk}
 
 
 def main():
@@ -511,7 +573,8 @@ def main():
         extra[name] = {"workload": edesc, "value": round(er["tok_s"], 1), "unit": "tokens/s",
                        "ms_per_step": round(er["ms"], 5), "rows": er["M"],
                        "roofline": er["roofline"], "layer_roofline": er["layer_roofline"],
-                       "stages": {k: v["us"] for k, v in er["stages"].items()}}
+                       "stages": {k: v["us"] for k, v in er["stages"].items()},
+                       "parts": er["parts"]}
         torch.cuda.empty_cache()
 
     result = {
@@ -530,6 +593,7 @@ def main():
         "graph_replay": r["graph_replay"],
         "per_call": r["per_call"],
         "standalone_call": r["standalone_call"],
+        "parts": r["parts"],
         "extra": extra,
     }
     log("timing the streaming read ...")
