@@ -65,7 +65,7 @@ struct AttnArgs {
   int dc_row0;   // first decode row
   int dc_slices;  // slices per kv head the grid provides (upper bound of P)
   int dc_pn;      // partial slots per q head = dc_slices + n
-  int dc_wgs;     // decode workgroups = min(free workgroups, dc_slices * nkv)
+  int dc_wgs;     // decode workgroups: min(free workgroups, dc_slices * nkv), >= units / NW
   float* dc_o;
   float* dc_ml;
   int merge_row0;  // first row the merge grid covers (chunk rows only when keys were split)
@@ -821,7 +821,9 @@ static hipError_t run_attention(AttnArgs& A, void* pf_ws, void* dc_ws, hipStream
     A.dc_slices = max(1, min(free_wgs * NW / (kDecSlotsPerWave * nkv),
                              decode_slice_cap(dec.n, nkv, dec.max_ctx)));
     A.dc_pn = A.dc_slices + dec.n;
-    A.dc_wgs = min(free_wgs, A.dc_slices * nkv);
+    // at most NW units per workgroup, however many kv heads a single slice
+    // per head gives (the second term only binds past ~free_wgs * NW heads)
+    A.dc_wgs = max(min(free_wgs, A.dc_slices * nkv), (A.dc_slices * nkv + NW - 1) / NW);
     A.dc_o = reinterpret_cast<float*>(dc_ws);
     A.dc_ml = A.dc_o + (size_t)nq * A.dc_pn * D;
   }
